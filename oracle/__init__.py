@@ -1,0 +1,112 @@
+"""Double-precision CPU oracle for causal GQA attention with RoPE.
+
+TEST INFRASTRUCTURE ONLY: the parity reference for the HIP library.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import this package.
+The product path never calls it and shares no code with it.
+
+The arithmetic lives in ``ne_oracle.c`` (plain C, double, OpenMP over KV groups); this module
+only builds it with gcc, loads it and marshals numpy arrays.  Every function is pinned by the
+tests in ``tests/test_oracle_*.py`` (closed forms, finite differences, independent library
+routines, invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ne_oracle.c")
+_LIB = os.path.join(_HERE, "libne_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics: no fast-math) into oracle/libne_oracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.ora_attn.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_double] + [dp] * 9 + [
+            ctypes.c_void_p, ctypes.c_int]
+        lib.ora_attn.restype = ctypes.c_int
+        lib.ora_rope.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp]
+        lib.ora_rope.restype = None
+        lib.ora_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _d(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return _load().ora_max_threads()
+
+
+def rope(x, theta, inverse=False, pos_offset=0):
+    """y = R_t x (or R_t^T x) for x of shape [B, H, T, D]; row t uses position t + pos_offset."""
+    x = _d(x)
+    B, H, T, D = x.shape
+    y = np.empty_like(x)
+    _load().ora_rope(B, H, T, D, float(theta), int(pos_offset), int(bool(inverse)), _ptr(x), _ptr(y))
+    return y
+
+
+def attention(q, k, v, do=None, theta=10000.0, scale=None, groups=None, nthreads=0):
+    """Causal GQA attention with RoPE in double.
+
+    q [B,Hq,T,D], k/v [B,Hkv,T,D], do [B,Hq,T,D] or None.
+    Returns (o, L) or (o, L, dq, dk, dv).  ``groups`` is an optional iterable of (b, g) pairs to
+    compute (the rest of every output is NaN); ``scale`` None means 1/sqrt(D); theta <= 0 means
+    no RoPE.
+    """
+    q, k, v = _d(q), _d(k), _d(v)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    o = np.full_like(q, np.nan)
+    L = np.full((B, Hq, T), np.nan)
+    mask = None
+    if groups is not None:
+        mask = np.zeros(B * Hkv, dtype=np.uint8)
+        for b, g in groups:
+            mask[b * Hkv + g] = 1
+    dq = dk = dv = None
+    if do is not None:
+        do = _d(do)
+        dq = np.full_like(q, np.nan)
+        dk = np.full_like(k, np.nan)
+        dv = np.full_like(v, np.nan)
+    rc = _load().ora_attn(B, Hq, Hkv, T, D, float(theta), float(scale or 0.0),
+                          _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o), _ptr(L),
+                          _ptr(dq), _ptr(dk), _ptr(dv),
+                          None if mask is None else mask.ctypes.data_as(ctypes.c_void_p),
+                          int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle failed with code %d" % rc)
+    if do is None:
+        return o, L
+    return o, L, dq, dk, dv
