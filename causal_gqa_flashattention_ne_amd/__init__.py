@@ -1,0 +1,227 @@
+"""Causal grouped-query FlashAttention with RoPE for MI355X (gfx950): thin Python binding.
+
+Every step of the computation runs in the HIP kernels of ``libne_attn.so`` (C ABI declared in
+``include/ne_attn.h``).  This module only marshals arguments: it checks tensor shapes/dtypes,
+allocates outputs with torch (device memory) and passes raw device pointers plus the current
+torch HIP stream through ctypes.  There is no fallback: if the library is missing, every call
+raises.
+
+Functions (same names as the C entry points, minus the ``ne_`` prefix):
+  rope_table(rows, D, theta, device)             -> float32 [rows, D/2, 2] (cached)
+  rope_apply(x, theta, inverse=False, pos_offset=0)
+  attn_fwd(q, k, v, rope_theta=10000.0, scale=None)          -> (o, lse)
+  attn_bwd(q, k, v, o, lse, do, rope_theta=10000.0, scale=None) -> (dq, dk, dv)
+and the allocation-free forms ``attn_fwd_into`` / ``attn_bwd_into`` used by the benchmark.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libne_attn.so")
+
+NE_OK = 0
+NE_DTYPE_F32 = 0
+NE_DTYPE_BF16 = 1
+ABI_VERSION = 1
+
+EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd",
+           "ne_attn_bwd_workspace_bytes", "ne_attn_bwd")
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
+
+
+class RopeParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pos_offset", ctypes.c_int32),
+                ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
+
+
+class NeError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__("%s failed: %s (code %d)" % (fn, msg, code))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libne_attn.so is not built (%s); run "
+                              "`python -m causal_gqa_flashattention_ne_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.ne_abi_version.restype = ctypes.c_int
+        L.ne_status_string.argtypes = [ctypes.c_int]
+        L.ne_status_string.restype = ctypes.c_char_p
+        L.ne_rope_table.argtypes = [i32, i32, ctypes.c_double, vp, vp]
+        L.ne_rope_apply.argtypes = [ctypes.POINTER(RopeParams), vp, vp, ctypes.c_int, vp]
+        L.ne_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp]
+        L.ne_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnParams)]
+        L.ne_attn_bwd_workspace_bytes.restype = sz
+        L.ne_attn_bwd.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
+        for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        if L.ne_abi_version() != ABI_VERSION:
+            raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != NE_OK:
+        raise NeError(fn, code, lib().ne_status_string(code).decode())
+
+
+def status_string(code: int) -> str:
+    return lib().ne_status_string(code).decode()
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NE_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return NE_DTYPE_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous ([B, H, T, D] row-major)" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+_tables = {}
+
+
+def rope_table(rows: int, D: int, theta: float, device) -> torch.Tensor:
+    """float32 [rows, D/2, 2] (cos, sin) table, computed by the library's fp64 kernel; cached."""
+    device = torch.device(device)
+    key = (int(rows), int(D), float(theta), str(device))
+    t = _tables.get(key)
+    if t is None:
+        t = torch.empty((rows, D // 2, 2), dtype=torch.float32, device=device)
+        _check("ne_rope_table", lib().ne_rope_table(rows, D, float(theta), _ptr(t), _stream(device)))
+        _tables[key] = t
+    return t
+
+
+def make_params(B, Hq, Hkv, T, D, dtype_code, scale=None, rope_cs=None) -> AttnParams:
+    p = AttnParams()
+    p.B, p.Hq, p.Hkv, p.T, p.D = B, Hq, Hkv, T, D
+    p.dtype = dtype_code
+    p.causal = 1
+    p.scale = float(scale) if scale else 0.0
+    p.rope_cs = rope_cs.data_ptr() if rope_cs is not None else None
+    p.rope_rows = rope_cs.shape[0] if rope_cs is not None else 0
+    return p
+
+
+def _params_for(q, k, rope_theta, scale):
+    _need(q, "q")
+    B, Hq, T, D = q.shape
+    _need(k, "k", dtype=q.dtype, device=q.device)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError("k has shape %s, incompatible with q %s" % (tuple(k.shape), tuple(q.shape)))
+    Hkv = k.shape[1]
+    cs = rope_table(T, D, rope_theta, q.device) if rope_theta and rope_theta > 0 else None
+    return make_params(B, Hq, Hkv, T, D, _dtype_code(q), scale, cs), cs
+
+
+def attn_fwd_into(p: AttnParams, q, k, v, o, lse, stream=None):
+    """Forward into preallocated o/lse (no allocation, no checks beyond the library's)."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_fwd", lib().ne_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st))
+
+
+def attn_bwd_into(p: AttnParams, q, k, v, o, lse, do, dq, dk, dv, ws, stream=None):
+    """Backward into preallocated dq/dk/dv using the workspace tensor ws (uint8)."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_bwd", lib().ne_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                            ws.numel() * ws.element_size(), st))
+
+
+def bwd_workspace_bytes(p: AttnParams) -> int:
+    return int(lib().ne_attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def attn_fwd(q, k, v, rope_theta: float = 10000.0, scale=None):
+    """Causal GQA attention forward.  q [B,Hq,T,D], k/v [B,Hkv,T,D] (float32 or bfloat16).
+
+    Returns (o [B,Hq,T,D] in q's dtype, lse [B,Hq,T] float32, natural log).  rope_theta <= 0 or
+    None disables RoPE; scale None means 1/sqrt(D).
+    """
+    p, _ = _params_for(q, k, rope_theta, scale)
+    _need(v, "v", shape=k.shape, dtype=q.dtype, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_into(p, q, k, v, o, lse)
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, do, rope_theta: float = 10000.0, scale=None):
+    """Backward of attn_fwd: returns (dq, dk, dv); dk/dv summed over each kv group's heads."""
+    p, _ = _params_for(q, k, rope_theta, scale)
+    _need(v, "v", shape=k.shape, dtype=q.dtype, device=q.device)
+    _need(o, "o", shape=q.shape, dtype=q.dtype, device=q.device)
+    _need(do, "do", shape=q.shape, dtype=q.dtype, device=q.device)
+    _need(lse, "lse", shape=q.shape[:3], dtype=torch.float32, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty(max(1, bwd_workspace_bytes(p)), dtype=torch.uint8, device=q.device)
+    attn_bwd_into(p, q, k, v, o, lse, do, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def rope_apply(x, theta: float = 10000.0, inverse: bool = False, pos_offset: int = 0, out=None):
+    """y = R x (or R^T x) for x [B, H, T, D]; row t uses position t + pos_offset.  out may be x."""
+    _need(x, "x")
+    B, H, T, D = x.shape
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", shape=x.shape, dtype=x.dtype, device=x.device)
+    cs = rope_table(T + pos_offset, D, theta, x.device)
+    rp = RopeParams()
+    rp.B, rp.H, rp.T, rp.D = B, H, T, D
+    rp.dtype = _dtype_code(x)
+    rp.pos_offset = pos_offset
+    rp.rope_cs = cs.data_ptr()
+    rp.rope_rows = cs.shape[0]
+    _check("ne_rope_apply", lib().ne_rope_apply(ctypes.byref(rp), _ptr(x), _ptr(y), int(bool(inverse)),
+                                                _stream(x.device)))
+    return y
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

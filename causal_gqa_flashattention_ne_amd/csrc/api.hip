@@ -1,0 +1,133 @@
+// api.hip -- the extern "C" entry points declared in include/ne_attn.h: argument validation
+// (before any launch) and dispatch on (dtype, head_dim) to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ne_attn.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr long kMaxElems = 0x7fffffffL;   // element counts index with 32-bit grid math
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_attn(const ne_attn_params* p) {
+    if (!p) return NE_ERR_NULL;
+    if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->T <= 0 || p->D <= 0) return NE_ERR_SHAPE;
+    if (p->Hq % p->Hkv != 0) return NE_ERR_SHAPE;
+    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
+    if (p->dtype != NE_DTYPE_F32 && p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
+    if (p->causal != 1) return NE_ERR_UNSUPPORTED;
+    if ((long)p->B * p->Hq * p->T * p->D > kMaxElems) return NE_ERR_SHAPE;
+    if (!isfinite(p->scale)) return NE_ERR_SHAPE;
+    if (p->rope_cs) {
+        if (p->rope_rows < p->T) return NE_ERR_SHAPE;
+        if (!aligned16(p->rope_cs)) return NE_ERR_ALIGN;
+    }
+    return NE_OK;
+}
+
+float eff_scale(const ne_attn_params* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D); }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* x : ps)
+        if (!x) return NE_ERR_NULL;
+    for (const void* x : ps)
+        if (!aligned16(x)) return NE_ERR_ALIGN;
+    return NE_OK;
+}
+
+size_t delta_bytes(const ne_attn_params* p) {
+    size_t n = (size_t)p->B * p->Hq * p->T * sizeof(float);
+    return (n + 255) & ~(size_t)255;
+}
+
+template <typename F>
+int dispatch(int dtype, int D, F&& f) {
+    hipError_t e;
+    if (dtype == NE_DTYPE_BF16) e = D == 64 ? f(ne::bf16{}, std::integral_constant<int, 64>{})
+                                            : f(ne::bf16{}, std::integral_constant<int, 32>{});
+    else e = D == 64 ? f(float{}, std::integral_constant<int, 64>{}) : f(float{}, std::integral_constant<int, 32>{});
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ne_abi_version(void) { return NE_ABI_VERSION; }
+
+const char* ne_status_string(int status) {
+    switch (status) {
+        case NE_OK: return "ok";
+        case NE_ERR_NULL: return "a required pointer is NULL";
+        case NE_ERR_SHAPE: return "invalid shape (size <= 0, Hq % Hkv != 0, too large, or rope table too short)";
+        case NE_ERR_UNSUPPORTED: return "unsupported configuration (head_dim not 32/64, dtype, or causal != 1)";
+        case NE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case NE_ERR_WORKSPACE: return "workspace too small";
+        case NE_ERR_HIP: return "HIP runtime error on launch";
+        default: return "unknown status";
+    }
+}
+
+int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream) {
+    if (!cs) return NE_ERR_NULL;
+    if (rows <= 0 || D <= 0 || (D % 2) != 0 || !(theta > 0.0) || !isfinite(theta)) return NE_ERR_SHAPE;
+    if ((long)rows * D > kMaxElems) return NE_ERR_SHAPE;
+    if (!aligned16(cs)) return NE_ERR_ALIGN;
+    return ne::launch_rope_table(rows, D, theta, cs, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? NE_OK : NE_ERR_HIP;
+}
+
+int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream) {
+    if (!p) return NE_ERR_NULL;
+    if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->D <= 0 || p->pos_offset < 0) return NE_ERR_SHAPE;
+    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
+    if (p->dtype != NE_DTYPE_F32 && p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
+    if ((long)p->B * p->H * p->T * p->D > kMaxElems) return NE_ERR_SHAPE;
+    if ((long)p->T + p->pos_offset > p->rope_rows) return NE_ERR_SHAPE;
+    if (int rc = check_ptrs({x, y, p->rope_cs})) return rc;
+    ne::RopeArgs a{x, y, p->rope_cs, p->B * p->H * p->T, p->T, p->pos_offset, inverse};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        return ne::launch_rope<decltype(t), decltype(d)::value>(a, s);
+    });
+}
+
+int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
+                float* lse, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (int rc = check_ptrs({q, k, v, o, lse})) return rc;
+    ne::FwdArgs a{q, k, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        return ne::launch_fwd<decltype(t), decltype(d)::value>(a, s);
+    });
+}
+
+size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
+    if (check_attn(p) != NE_OK) return 0;
+    return delta_bytes(p) + (size_t)p->B * p->Hq * p->T * p->D * sizeof(float);
+}
+
+int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (int rc = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return rc;
+    if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
+    float* delta = static_cast<float*>(workspace);
+    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
+    ne::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, p->rope_cs,
+                  p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        return ne::launch_bwd<decltype(t), decltype(d)::value>(a, s);
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// kernels.hpp -- argument blocks and launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ne {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const float* rope_cs;   // [T][D/2][2] or nullptr
+    int B, Hq, Hkv, T;
+    float scale;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;           // workspace: [B, Hq, T] rowsum(dO * O)
+    float* dq_acc;          // workspace: [B, Hq, T, D] float32 accumulator of rotated dQ
+    const float* rope_cs;
+    int B, Hq, Hkv, T;
+    float scale;
+};
+
+struct RopeArgs {
+    const void* x;
+    void* y;
+    const float* rope_cs;
+    int rows;               // B * H * T
+    int T;
+    int pos_offset;
+    int inverse;
+};
+
+template <typename T, int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+template <typename T, int D> hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_rope_table(int rows, int D, double theta, float* cs, hipStream_t stream);
+
+}  // namespace ne

@@ -1,0 +1,126 @@
+/*
+ * ne_attn.h -- C ABI of the MI355X (gfx950) causal grouped-query FlashAttention library.
+ *
+ * The operation is the attention of a small decoder-only GPT as the NanoEuler pages describe it:
+ * RoPE on queries and keys, grouped-query attention (a smaller set of key/value heads, each
+ * shared by a contiguous group of query heads), causal self-attention, computed with tiling and
+ * an online softmax so that the T x T score matrix is never stored, with a hand-written backward
+ * pass.  (agentlenshq page "NanoEuler: C와 CUDA로 밑바닥부터 구축한 GPT-2 규모의 LLM", sections
+ * "기술 사양" and "커널 구현"; byte-level GPT page "Tiny hackable CUDA language model
+ * implementation", section "Core Mechanics"; ai-paper-delta NanoEuler page, "Core Mechanics".)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Layout: every activation is [B, H, T, D], contiguous, row-major (D fastest).
+ *    q, o, dout, dq: H = Hq.  k, v, dk, dv: H = Hkv.  lse: [B, Hq, T] float32.
+ *  * Query head h reads key/value head h / (Hq / Hkv).
+ *  * Causal mask: query i sees keys j <= i (its own position included).
+ *  * RoPE: adjacent pairs (x[2i], x[2i+1]) at position t are rotated by t * theta^(-2i/D):
+ *    (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).  The rotation angles come from a table made
+ *    by ne_rope_table (cos/sin evaluated in double, stored as float32).
+ *  * Scores S_ij = scale * <R_i q_i, R_j k_j>; lse_i = ln sum_{j<=i} exp(S_ij) (natural log).
+ *  * Element types: NE_DTYPE_F32 (float32 in/out, float32 arithmetic) or NE_DTYPE_BF16 (bfloat16
+ *    in/out, bf16 matrix-core products with float32 accumulation).  lse and the workspace are
+ *    always float32.
+ *  * Memory: every pointer is device memory owned by the caller, 16-byte aligned.  The library
+ *    allocates nothing and keeps no state beyond a cached device-property query.  Inputs are
+ *    never written; outputs are fully overwritten (never accumulated into).
+ *  * Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are asynchronous and
+ *    never synchronise the host; device-side faults surface at the caller's next synchronisation.
+ *  * Errors: 0 (NE_OK) or a negative NE_ERR_* code.  Arguments are validated before anything is
+ *    launched; on an error nothing is launched and no output is touched.  No C++ exception
+ *    crosses this interface.
+ */
+#ifndef NE_ATTN_H
+#define NE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NE_ABI_VERSION 1
+
+enum {
+    NE_OK = 0,
+    NE_ERR_NULL = -1,        /* a required pointer is NULL */
+    NE_ERR_SHAPE = -2,       /* a size <= 0, Hq % Hkv != 0, rope table too short, ... */
+    NE_ERR_UNSUPPORTED = -3, /* head_dim not in {32, 64}, unknown dtype, causal != 1 */
+    NE_ERR_ALIGN = -4,       /* a pointer that is not 16-byte aligned */
+    NE_ERR_WORKSPACE = -5,   /* workspace smaller than ne_attn_bwd_workspace_bytes() */
+    NE_ERR_HIP = -6          /* the HIP runtime reported an error on launch */
+};
+
+enum { NE_DTYPE_F32 = 0, NE_DTYPE_BF16 = 1 };
+
+typedef struct ne_attn_params {
+    int32_t B, Hq, Hkv, T, D;   /* batch, query heads, kv heads, sequence length, head_dim */
+    int32_t dtype;              /* NE_DTYPE_F32 or NE_DTYPE_BF16 */
+    int32_t causal;             /* must be 1 */
+    float scale;                /* softmax scale; <= 0 means 1/sqrt(D) */
+    const float* rope_cs;       /* device [rope_rows][D/2][2] (cos, sin) table, or NULL = no RoPE */
+    int32_t rope_rows;          /* rows in rope_cs; must be >= T when rope_cs != NULL */
+} ne_attn_params;
+
+typedef struct ne_rope_params {
+    int32_t B, H, T, D;
+    int32_t dtype;              /* NE_DTYPE_F32 or NE_DTYPE_BF16 */
+    int32_t pos_offset;         /* row t is rotated with the table row t + pos_offset (>= 0) */
+    const float* rope_cs;       /* device [rope_rows][D/2][2] */
+    int32_t rope_rows;          /* must be >= T + pos_offset */
+} ne_rope_params;
+
+/* NE_ABI_VERSION of the loaded library. */
+int ne_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ne_status_string(int status);
+
+/*
+ * Fill the RoPE table: cs[t][i] = (cos(t w_i), sin(t w_i)), w_i = theta^(-2i/D), for
+ * t < rows and i < D/2, evaluated in double on the device and rounded to float32.
+ * cs: device, rows * D * sizeof(float) bytes, written.  D even and >= 2, rows >= 1, theta > 0.
+ * (RoPE on queries and keys: agentlenshq NanoEuler page, "기술 사양".)
+ */
+int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream);
+
+/*
+ * y = R x (inverse == 0) or y = R^T x (inverse != 0) for x, y of shape [B, H, T, D] in dtype;
+ * row t uses the table row t + pos_offset.  x == y (in place) is allowed; other overlap is not.
+ * D must be in {32, 64}.  (Rotary embedding of queries and keys: agentlenshq NanoEuler page,
+ * "기술 사양"; byte-level GPT page, "Core Mechanics".)
+ */
+int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream);
+
+/*
+ * Forward: o = softmax_causal(scale * (R q)(R k)^T) v and lse (natural log), per query head,
+ * with kv head h / (Hq/Hkv).  q [B,Hq,T,D], k/v [B,Hkv,T,D], o [B,Hq,T,D] in dtype;
+ * lse [B,Hq,T] float32.  Tiled with an online softmax: no T x T buffer exists at any point
+ * (agentlenshq NanoEuler page, "커널 구현").
+ */
+int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
+                float* lse, void* stream);
+
+/* Bytes of float32 workspace that ne_attn_bwd needs for these parameters (0 on a bad shape). */
+size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);
+
+/*
+ * Backward of ne_attn_fwd for the upstream gradient dout (hand-written backward: ai-paper-delta
+ * NanoEuler page, "Core Mechanics"; agentlenshq NanoEuler page, "검증 및 안정성").
+ * Inputs: q, k, v, o (the forward output), lse (the forward lse), dout [B,Hq,T,D].
+ * Outputs: dq [B,Hq,T,D], dk, dv [B,Hkv,T,D], all in dtype.  dq and dk are gradients with
+ * respect to the un-rotated q and k the caller passed; dk and dv are summed over the query heads
+ * of each kv group.  workspace: device, >= ne_attn_bwd_workspace_bytes(p) bytes, owned by the
+ * caller; its contents on entry are ignored and on exit are unspecified.
+ */
+int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NE_ATTN_H */

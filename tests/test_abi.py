@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/ne_attn.h
+declares, and rejects bad arguments with the documented codes before anything is launched.
+
+The pointers passed below are never dereferenced: every call here fails validation, which runs
+before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_gqa_flashattention_ne_amd as ne
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ne_attn.h")
+
+ALIGNED = 0x10000          # fake, 16-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ne_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(ne.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ne.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.ne_abi_version() == ne.ABI_VERSION
+    assert ne.status_string(0) == "ok"
+    for code in range(-6, 0):
+        assert ne.status_string(code) != "unknown status"
+    assert ne.status_string(-99) == "unknown status"
+
+
+def params(**kw):
+    base = dict(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_BF16)
+    base.update(kw)
+    return ne.make_params(**base)
+
+
+def fwd(p, q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED):
+    vp = ctypes.c_void_p
+    return ne.lib().ne_attn_fwd(ctypes.byref(p), vp(q), vp(k), vp(v), vp(o), vp(lse), None)
+
+
+def bwd(p, ws_bytes=1 << 30, ptrs=None):
+    vp = ctypes.c_void_p
+    ptrs = ptrs or [ALIGNED] * 10
+    return ne.lib().ne_attn_bwd(ctypes.byref(p), *[vp(x) for x in ptrs], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=3, Hkv=2), -2),
+    (dict(B=0), -2),
+    (dict(T=-1), -2),
+    (dict(Hkv=0), -2),
+    (dict(D=48), -3),
+    (dict(D=128), -3),
+    (dict(dtype_code=7), -3),
+    (dict(B=1 << 20, Hq=64, Hkv=1, T=1 << 10), -2),
+])
+def test_forward_rejects_bad_shapes(kw, code):
+    assert fwd(params(**kw)) == code
+    assert bwd(params(**kw)) == code
+    assert ne.lib().ne_attn_bwd_workspace_bytes(ctypes.byref(params(**kw))) == 0
+
+
+def test_causal_must_be_one():
+    p = params()
+    p.causal = 0
+    assert fwd(p) == -3
+
+
+def test_null_and_misaligned_pointers():
+    p = params()
+    assert fwd(p, q=0) == -1
+    assert fwd(p, lse=0) == -1
+    assert fwd(p, v=MISALIGNED) == -4
+    ptrs = [ALIGNED] * 10
+    ptrs[9] = 0
+    assert bwd(p, ptrs=ptrs) == -1
+    ptrs[9] = MISALIGNED
+    assert bwd(p, ptrs=ptrs) == -4
+
+
+def test_rope_table_rows_checked():
+    p = params()
+    p.rope_cs = ALIGNED
+    p.rope_rows = 15          # T = 16
+    assert fwd(p) == -2
+    p.rope_cs = MISALIGNED
+    p.rope_rows = 16
+    assert fwd(p) == -4
+
+
+def test_workspace_size_and_check():
+    p = params(B=2, Hq=4, Hkv=2, T=16, D=64)
+    need = ne.bwd_workspace_bytes(p)
+    delta = 2 * 4 * 16 * 4
+    assert need == ((delta + 255) // 256) * 256 + 2 * 4 * 16 * 64 * 4
+    assert bwd(p, ws_bytes=need - 1) == -5
+
+
+def test_rope_entry_points_validate():
+    L = ne.lib()
+    vp = ctypes.c_void_p
+    assert L.ne_rope_table(0, 64, 10000.0, vp(ALIGNED), None) == -2
+    assert L.ne_rope_table(16, 63, 10000.0, vp(ALIGNED), None) == -2
+    assert L.ne_rope_table(16, 64, 0.0, vp(ALIGNED), None) == -2
+    assert L.ne_rope_table(16, 64, 10000.0, None, None) == -1
+    assert L.ne_rope_table(16, 64, 10000.0, vp(MISALIGNED), None) == -4
+    rp = ne.RopeParams()
+    rp.B, rp.H, rp.T, rp.D, rp.dtype, rp.pos_offset, rp.rope_cs, rp.rope_rows = 1, 2, 8, 64, 1, 4, ALIGNED, 11
+    assert L.ne_rope_apply(ctypes.byref(rp), vp(ALIGNED), vp(ALIGNED), 0, None) == -2   # 8 + 4 > 11
+    rp.rope_rows = 12
+    assert L.ne_rope_apply(ctypes.byref(rp), vp(MISALIGNED), vp(ALIGNED), 0, None) == -4
+    rp.D = 16
+    assert L.ne_rope_apply(ctypes.byref(rp), vp(ALIGNED), vp(ALIGNED), 0, None) == -3
+    rp.D, rp.pos_offset = 64, -1
+    assert L.ne_rope_apply(ctypes.byref(rp), vp(ALIGNED), vp(ALIGNED), 0, None) == -2
