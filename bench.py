@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: causal GQA attention forward + backward on one MI355X, through the C ABI.
+
+A step is one pass of the whole hot path over one batch of synthetic input: RoPE-fused forward
+(O and L) then the backward (delta preprocess and the main kernel: dQ, dK, dV), for every layer
+of the workload.  Inputs are resident in HBM before the timed region; outputs and workspace are
+preallocated; nothing is allocated or copied inside it.
+
+Prints ONE JSON line.  value = whole-job algorithmic TFLOP/s with the causal pairs counted exactly:
+14 * D * B * Hq * T(T+1)/2 per layer (forward 4*D, backward 10*D per pair).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix peaks
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal GQA attention fwd+bwd TFLOP/s (T=512,d=64); % of MI355X MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
+    return ap.parse_args()
+
+
+def kernel_bytes(w, elem):
+    """Algorithmic HBM bytes per layer (every tensor read or written once)."""
+    q = w.B * w.Hq * w.T * w.D * elem
+    kv = w.B * w.Hkv * w.T * w.D * elem
+    rows = w.B * w.Hq * w.T * 4
+    return {
+        "fwd": q + 2 * kv + q + rows,                     # Q, K, V in; O, L out
+        "bwd_pre": 2 * q + rows,                          # O, dO in; delta out
+        "bwd_main": q + 2 * kv + q + 2 * rows + q + 2 * kv,  # Q, K, V, dO, L, delta in; dQ, dK, dV out
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the attention path is sharded by (batch, kv group) with no "
+              "communication, so each GPU would run this same step on its share; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_gqa_flashattention_ne_amd as ne
+    import gen
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.WORKLOADS[args.workload]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+
+    # ---- inputs resident in HBM, outputs and workspace preallocated ----
+    layers = []
+    host_inputs = []
+    for layer in range(w.layers):
+        q, k, v, do = gen.layer_inputs(w, layer)
+        if layer == 0:
+            host_inputs = (q, k, v, do)
+        t = [torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (q, k, v, do)]
+        layers.append(t)
+    cs = ne.rope_table(w.T, w.D, w.theta, dev)
+    p = ne.make_params(w.B, w.Hq, w.Hkv, w.T, w.D, ne._dtype_code(layers[0][0]), None, cs)
+    ws = torch.empty(ne.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    outs = []
+    for (q, k, v, do) in layers:
+        outs.append((torch.empty_like(q), torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev),
+                     torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)))
+    stream = torch.cuda.current_stream(dev)
+    st = ne.ctypes.c_void_p(stream.cuda_stream)
+
+    def step(ev=None):
+        for li, ((q, k, v, do), (o, lse, dq, dk, dv)) in enumerate(zip(layers, outs)):
+            if ev is not None:
+                ev[0][li].record(stream)
+            ne.attn_fwd_into(p, q, k, v, o, lse, st)
+            if ev is not None:
+                ev[1][li].record(stream)
+            ne.attn_bwd_preprocess_into(p, o, do, ws, st)
+            if ev is not None:
+                ev[2][li].record(stream)
+            ne.attn_bwd_main_into(p, q, k, v, lse, do, dq, dk, dv, ws, st)
+            if ev is not None:
+                ev[3][li].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps between two events on the launch stream ----
+    K = args.steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(K):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+
+    # ---- the same K steps again with an event pair around every kernel call (same stream) ----
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    dur = {"fwd": [], "bwd_pre": [], "bwd_main": []}
+    for i in range(K):
+        for li in range(w.layers):
+            e = evs[i]
+            dur["fwd"].append(e[0][li].elapsed_time(e[1][li]))
+            dur["bwd_pre"].append(e[1][li].elapsed_time(e[2][li]))
+            dur["bwd_main"].append(e[2][li].elapsed_time(e[3][li]))
+    avg_us = {kname: 1000.0 * float(np.mean(v)) for kname, v in dur.items()}
+
+    pairs = w.causal_pairs
+    flop_layer = 14.0 * w.D * pairs
+    value = flop_layer * w.layers / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # ---- roofline of the dominant kernel ----
+    kflops = {"fwd": 4.0 * w.D * pairs, "bwd_pre": 0.0, "bwd_main": 10.0 * w.D * pairs}
+    kbytes = kernel_bytes(w, elem)
+    dom = max(avg_us, key=lambda kname: avg_us[kname])
+    t_s = avg_us[dom] * 1e-6
+    t_mfma = kflops[dom] / (peak * 1e12)
+    t_hbm = kbytes[dom] / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": kflops[dom] / t_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kbytes[dom] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_us"] = avg_us[dom]
+    roof["algorithmic_flop"] = kflops[dom]
+    roof["algorithmic_bytes"] = kbytes[dom]
+    roof["mfma_tflops"] = kflops[dom] / t_s / 1e12
+    roof["hbm_gbs"] = kbytes[dom] / t_s / 1e9
+
+    # ---- CPU baseline: the oracle on the host cores (rank 0, N = 1 only) ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        q, k, v, do = host_inputs
+        groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+        # bounded sample: whole kv groups of layer 0, up to ~10-30 s of CPU work
+        est_core_s_per_group = 1.0e-9 * 14 * w.D * w.G * w.T * (w.T + 1) / 2 / 1.2   # ~1.2 GFLOP/s/core
+        budget = 20.0 * threads
+        n = max(1, min(len(groups), int(budget / max(est_core_s_per_group, 1e-9))))
+        sample = groups[:n]
+        used = min(threads, n)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, do, theta=w.theta, groups=sample, nthreads=used)
+        dt = time.perf_counter() - t0
+        sample_flop = 14.0 * w.D * len(sample) * w.G * w.T * (w.T + 1) / 2
+        cpu = {"value": sample_flop / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+               "sample": "%d of %d (batch, kv group) units of layer 0 (all %d query heads each, all T=%d "
+                         "positions), forward+backward in double, %.2f s wall" %
+                         (len(sample), len(groups), w.G, w.T, dt)}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64 normals; shapes of the workload)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
+                   "layers": w.layers, "causal": True, "rope_theta": w.theta, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / peak,
+        "peak_tflops": peak,
+        "kernel_avg_us": avg_us,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,7 @@ NE_DTYPE_BF16 = 1
 ABI_VERSION = 1
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd",
-           "ne_attn_bwd_workspace_bytes", "ne_attn_bwd")
+           "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main")
 
 
 class AttnParams(ctypes.Structure):
@@ -73,7 +73,10 @@ def lib():
         L.ne_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnParams)]
         L.ne_attn_bwd_workspace_bytes.restype = sz
         L.ne_attn_bwd.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
-        for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd"):
+        L.ne_attn_bwd_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, sz, vp]
+        L.ne_attn_bwd_main.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 8 + [vp, sz, vp]
+        for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
+                  "ne_attn_bwd_main"):
             getattr(L, f).restype = ctypes.c_int
         if L.ne_abi_version() != ABI_VERSION:
             raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
@@ -170,6 +173,19 @@ def attn_bwd_into(p: AttnParams, q, k, v, o, lse, do, dq, dk, dv, ws, stream=Non
     _check("ne_attn_bwd", lib().ne_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                             ws.numel() * ws.element_size(), st))
+
+
+def attn_bwd_preprocess_into(p: AttnParams, o, do, ws, stream=None):
+    st = stream if stream is not None else _stream(o.device)
+    _check("ne_attn_bwd_preprocess", lib().ne_attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(ws),
+                                                                  ws.numel() * ws.element_size(), st))
+
+
+def attn_bwd_main_into(p: AttnParams, q, k, v, lse, do, dq, dk, dv, ws, stream=None):
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_bwd_main", lib().ne_attn_bwd_main(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse),
+                                                      _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                                      ws.numel() * ws.element_size(), st))
 
 
 def bwd_workspace_bytes(p: AttnParams) -> int:

@@ -114,20 +114,55 @@ size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     return delta_bytes(p) + (size_t)p->B * p->Hq * p->T * p->D * sizeof(float);
 }
 
+namespace {
+int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, ne::BwdArgs* a) {
+    if (int rc = check_attn(p)) return rc;
+    if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
+    float* delta = static_cast<float*>(workspace);
+    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
+    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, p->rope_cs,
+                     p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
+    return NE_OK;
+}
+}  // namespace
+
+int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* o, const void* dout, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (int rc = check_ptrs({o, dout, workspace})) return rc;
+    ne::BwdArgs a;
+    if (int rc = bwd_args(p, nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+                          workspace, workspace_bytes, &a)) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        return ne::launch_bwd_pre<decltype(t), decltype(d)::value>(a, s);
+    });
+}
+
+int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, const void* v,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (int rc = check_ptrs({q, k, v, lse, dout, dq, dk, dv, workspace})) return rc;
+    ne::BwdArgs a;
+    if (int rc = bwd_args(p, q, k, v, nullptr, lse, dout, dq, dk, dv, workspace, workspace_bytes, &a))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        return ne::launch_bwd_main<decltype(t), decltype(d)::value>(a, s);
+    });
+}
+
 int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const void* v, const void* o,
                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, void* stream) {
     if (int rc = check_attn(p)) return rc;
     if (int rc = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return rc;
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    float* delta = static_cast<float*>(workspace);
-    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
-    ne::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, p->rope_cs,
-                  p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
-        return ne::launch_bwd<decltype(t), decltype(d)::value>(a, s);
-    });
+    if (int rc = ne_attn_bwd_preprocess(p, o, dout, workspace, workspace_bytes, stream)) return rc;
+    return ne_attn_bwd_main(p, q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -318,41 +318,43 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 }  // namespace
 
 template <typename T, int D>
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
     constexpr int VEC = 16 / sizeof(T);
-    const long rows = (long)a.B * a.Hq * a.T;
-    {
-        const long threads = rows * (D / VEC);
-        hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, a);
-    }
-    {
-        using L = BwdSmem<T, D>;
-        // opt in to more than 64 KiB of dynamic LDS, once per device
-        static bool attr_set[64] = {};
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<T, D>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
-            if (e != hipSuccess) return e;
-            if (dev >= 0 && dev < 64) attr_set[dev] = true;
-        }
-        const long blocks = (long)((a.T + kBwdBN - 1) / kBwdBN) * a.B * a.Hkv;
-        hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), L::BYTES, stream, a);
-    }
-    {
-        const long threads = rows * (D / 4);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, a);
-    }
+    const long threads = (long)a.B * a.Hq * a.T * (D / VEC);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd<bf16, 32>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd<float, 64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd<float, 32>(const BwdArgs&, hipStream_t);
+template <typename T, int D>
+hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
+    using L = BwdSmem<T, D>;
+    // opt in to more than 64 KiB of dynamic LDS, once per device
+    static bool attr_set[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<T, D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    const long blocks = (long)((a.T + kBwdBN - 1) / kBwdBN) * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), L::BYTES, stream, a);
+    const long threads = (long)a.B * a.Hq * a.T * (D / 4);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template hipError_t launch_bwd_pre<bf16, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_main<bf16, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_pre<bf16, 32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_main<bf16, 32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_pre<float, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_main<float, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_pre<float, 32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_main<float, 32>(const BwdArgs&, hipStream_t);
 
 }  // namespace ne

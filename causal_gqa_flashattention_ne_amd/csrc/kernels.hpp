@@ -45,7 +45,8 @@ struct RopeArgs {
 };
 
 template <typename T, int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-template <typename T, int D> hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int D, double theta, float* cs, hipStream_t stream);
 
