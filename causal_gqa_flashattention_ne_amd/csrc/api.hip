@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/ne_attn.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -111,7 +113,10 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
 
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
-    return delta_bytes(p) + (size_t)p->B * p->Hq * p->T * p->D * sizeof(float);
+    const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
+    // float32: delta | float32 dQ accumulator;  bf16: delta | rotated Q | rotated K (bf16)
+    if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
+    return delta_bytes(p) + qe * sizeof(float);
 }
 
 namespace {
@@ -120,24 +125,37 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
              size_t workspace_bytes, ne::BwdArgs* a) {
     if (int rc = check_attn(p)) return rc;
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    float* delta = static_cast<float*>(workspace);
-    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
-    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, p->rope_cs,
+    char* ws = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(ws);
+    const size_t qe = (size_t)p->B * p->Hq * p->T * p->D;
+    float* dq_acc = nullptr;
+    void* qrot = nullptr;
+    void* krot = nullptr;
+    if (p->dtype == NE_DTYPE_BF16) {
+        qrot = ws + delta_bytes(p);
+        krot = ws + delta_bytes(p) + ((qe * 2 + 255) & ~(size_t)255);
+    } else {
+        dq_acc = reinterpret_cast<float*>(ws + delta_bytes(p));
+    }
+    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, qrot, krot, p->rope_cs,
                      p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
     return NE_OK;
 }
 }  // namespace
 
-int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* o, const void* dout, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k, const void* o,
+                           const void* dout, void* workspace, size_t workspace_bytes, void* stream) {
     if (int rc = check_attn(p)) return rc;
-    if (int rc = check_ptrs({o, dout, workspace})) return rc;
+    if (int rc = check_ptrs({q, k, o, dout, workspace})) return rc;
     ne::BwdArgs a;
-    if (int rc = bwd_args(p, nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+    if (int rc = bwd_args(p, q, k, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
                           workspace, workspace_bytes, &a)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
-        return ne::launch_bwd_pre<decltype(t), decltype(d)::value>(a, s);
+        using T = decltype(t);
+        constexpr int DD = decltype(d)::value;
+        if constexpr (std::is_same<T, ne::bf16>::value) return ne::launch_bwd_pre_bf16<DD>(a, s);
+        else return ne::launch_bwd_pre<T, DD>(a, s);
     });
 }
 
@@ -151,7 +169,13 @@ int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, cons
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
-        return ne::launch_bwd_main<decltype(t), decltype(d)::value>(a, s);
+        using T = decltype(t);
+        constexpr int DD = decltype(d)::value;
+        if constexpr (std::is_same<T, ne::bf16>::value) {
+            return ne::launch_bwd_main_bf16<DD>(a, s);
+        } else {
+            return ne::launch_bwd_main<T, DD>(a, s);
+        }
     });
 }
 
@@ -161,7 +185,7 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
     if (int rc = check_attn(p)) return rc;
     if (int rc = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return rc;
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    if (int rc = ne_attn_bwd_preprocess(p, o, dout, workspace, workspace_bytes, stream)) return rc;
+    if (int rc = ne_attn_bwd_preprocess(p, q, k, o, dout, workspace, workspace_bytes, stream)) return rc;
     return ne_attn_bwd_main(p, q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 

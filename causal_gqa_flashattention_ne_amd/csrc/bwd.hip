@@ -342,12 +342,21 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
     }
     const long blocks = (long)((a.T + kBwdBN - 1) / kBwdBN) * a.B * a.Hkv;
     hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), L::BYTES, stream, a);
+    return launch_bwd_dq<T, D>(a, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
     const long threads = (long)a.B * a.Hq * a.T * (D / 4);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
+template hipError_t launch_bwd_dq<bf16, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<bf16, 32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<float, 64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<float, 32>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre<bf16, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main<bf16, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre<bf16, 32>(const BwdArgs&, hipStream_t);

@@ -28,7 +28,9 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* delta;           // workspace: [B, Hq, T] rowsum(dO * O)
-    float* dq_acc;          // workspace: [B, Hq, T, D] float32 accumulator of rotated dQ
+    float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
+    void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q, written by the preprocess
+    void* krot;             // workspace (bf16 path): [B, Hkv, T, D] rotated K, written by the preprocess
     const float* rope_cs;
     int B, Hq, Hkv, T;
     float scale;
@@ -47,6 +49,9 @@ struct RopeArgs {
 template <typename T, int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D> hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int D, double theta, float* cs, hipStream_t stream);
 
