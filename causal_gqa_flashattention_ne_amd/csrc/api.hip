@@ -107,7 +107,10 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
     ne::FwdArgs a{q, k, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
-        return ne::launch_fwd<decltype(t), decltype(d)::value>(a, s);
+        using T = decltype(t);
+        constexpr int DD = decltype(d)::value;
+        if constexpr (std::is_same<T, ne::bf16>::value) return ne::launch_fwd_bf16<DD>(a, s);
+        else return ne::launch_fwd<T, DD>(a, s);
     });
 }
 

@@ -157,7 +157,8 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.Hq / a.Hkv;
     const int j0 = jt * kTile;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform across the wave
     const int col = lane & 31, half = lane >> 5;
     const int kh = w & 1, qh = w >> 1;
     const int kloc = 32 * kh + col;
@@ -217,32 +218,42 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         const bf16* Gs = S.g[buf];
         const bool first = (i0 == j0);
         if (!(first && kh > qh)) {            // blocks wholly above the diagonal are skipped
-            f32x16 sacc, dp;
-            {
-                const bf16* qrow = &Qs[(32 * qh + col) * RS + 8 * half];
-                const bf16* grow = &Gs[(32 * qh + col) * RS + 8 * half];
-                sacc = M::mma(*reinterpret_cast<const bf16x8*>(qrow), kop[0], f32x16{});
-                dp = M::mma(*reinterpret_cast<const bf16x8*>(grow), vop[0], f32x16{});
+            // query / dO fragments first, then the two independent chains interleaved
+            bf16x8 qf[NCH], gf[NCH];
 #pragma unroll
-                for (int c = 1; c < NCH; ++c) {
-                    sacc = M::mma(*reinterpret_cast<const bf16x8*>(qrow + 16 * c), kop[c], sacc);
-                    dp = M::mma(*reinterpret_cast<const bf16x8*>(grow + 16 * c), vop[c], dp);
-                }
+            for (int c = 0; c < NCH; ++c) {
+                qf[c] = *reinterpret_cast<const bf16x8*>(&Qs[(32 * qh + col) * RS + 16 * c + 8 * half]);
+                gf[c] = *reinterpret_cast<const bf16x8*>(&Gs[(32 * qh + col) * RS + 16 * c + 8 * half]);
+            }
+            f32x16 sacc = M::mma(qf[0], kop[0], f32x16{});
+            f32x16 dp = M::mma(gf[0], vop[0], f32x16{});
+#pragma unroll
+            for (int c = 1; c < NCH; ++c) {
+                sacc = M::mma(qf[c], kop[c], sacc);
+                dp = M::mma(gf[c], vop[c], dp);
             }
             bf16x8 pb[2], sb[2];
             if (first && kh == qh)
                 kv_softmax<true>(sacc, dp, S.l[buf], S.dl[buf], sl2, kloc, 32 * qh, half, pb, sb);
             else
                 kv_softmax<false>(sacc, dp, S.l[buf], S.dl[buf], sl2, kloc, 32 * qh, half, pb, sb);
+            bf16x8 gt[2][NDT], qtf[2][NDT];
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 const int kb0 = 32 * qh + 16 * pc + 4 * half;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    dvt[dt] = M::mma(tr_frag(Gs, RS, 32 * dt, kb0, kb0 + 8, lane), pb[pc], dvt[dt]);
-                    dkt[dt] = M::mma(tr_frag(Qs, RS, 32 * dt, kb0, kb0 + 8, lane), sb[pc], dkt[dt]);
+                    gt[pc][dt] = tr_frag(Gs, RS, 32 * dt, kb0, kb0 + 8, lane);
+                    qtf[pc][dt] = tr_frag(Qs, RS, 32 * dt, kb0, kb0 + 8, lane);
                 }
             }
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    dvt[dt] = M::mma(gt[pc][dt], pb[pc], dvt[dt]);
+                    dkt[dt] = M::mma(qtf[pc][dt], sb[pc], dkt[dt]);
+                }
         }
         if (more) store(buf ^ 1, ni0);
         __syncthreads();
@@ -296,7 +307,8 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     const int i0 = qt * kQBlk;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform across the wave
     const int col = lane & 31, half = lane >> 5;
     const int wq0 = i0 + 32 * w;            // wave's first query
     const int qrow = wq0 + col;             // this lane's query
@@ -339,19 +351,28 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
+            // key / value fragments first, then four independent chains interleaved
+            bf16x8 kf[2][NCH], vf[2][NCH];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + col) * RS + 16 * c + 8 * half]);
+                    vf[kt][c] = *reinterpret_cast<const bf16x8*>(&Vs[(32 * kt + col) * RS + 16 * c + 8 * half]);
+                }
             f32x16 sT[2], dpT[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const bf16* kr = &Ks[(32 * kt + col) * RS + 8 * half];
-                const bf16* vr = &Vs[(32 * kt + col) * RS + 8 * half];
-                sT[kt] = M::mma(*reinterpret_cast<const bf16x8*>(kr), qop[0], f32x16{});
-                dpT[kt] = M::mma(*reinterpret_cast<const bf16x8*>(vr), gop[0], f32x16{});
-#pragma unroll
-                for (int c = 1; c < NCH; ++c) {
-                    sT[kt] = M::mma(*reinterpret_cast<const bf16x8*>(kr + 16 * c), qop[c], sT[kt]);
-                    dpT[kt] = M::mma(*reinterpret_cast<const bf16x8*>(vr + 16 * c), gop[c], dpT[kt]);
-                }
+                sT[kt] = M::mma(kf[kt][0], qop[0], f32x16{});
+                dpT[kt] = M::mma(vf[kt][0], gop[0], f32x16{});
             }
+#pragma unroll
+            for (int c = 1; c < NCH; ++c)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    sT[kt] = M::mma(kf[kt][c], qop[c], sT[kt]);
+                    dpT[kt] = M::mma(vf[kt][c], gop[c], dpT[kt]);
+                }
             // dS'^T = P' (dP^T - delta), packed as B operands (4 chunks of 16 keys)
             bf16x8 sb[4];
             const bool diag = j0 + kTile - 1 > wq0;
@@ -373,13 +394,17 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                     else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             // dQ~^T (D x 32 queries) += K~^T dS'^T  (K = the tile's keys, accumulator order)
+            bf16x8 ktf[4][NDT];
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc) {
                 const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    dqt[dt] = M::mma(tr_frag(Ks, RS, 32 * dt, kb0, kb0 + 8, lane), sb[pc], dqt[dt]);
+                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag(Ks, RS, 32 * dt, kb0, kb0 + 8, lane);
             }
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
         }
         if (more) pf.store(S.k[buf ^ 1], S.v[buf ^ 1], tid);
         __syncthreads();

@@ -1,0 +1,274 @@
+// fwd_bf16.hip -- bf16 causal GQA FlashAttention forward for gfx950 (float32 path: fwd.hip).
+//
+// Tiling plus an online softmax, so the T x T matrix is never stored (agentlenshq NanoEuler page,
+// section "커널 구현"); RoPE is applied to queries and keys as they are loaded (same page,
+// "기술 사양").
+//
+// A workgroup owns 128 queries of one (batch, query head); wave w owns queries 32w..32w+31,
+// one lane per query.  Key/value tiles of 64 rows stream through LDS, double-buffered: the next
+// tile is loaded (clamped, unconditional loads, so nothing waits on them early), the keys are
+// rotated in registers and both tiles stored row-major with 16-byte writes after the current
+// tile's products.  Only tiles at or before the block's last query are visited.
+//   S^T = K~ Q~^T        (A = key rows from LDS, B = this lane's rotated query in registers)
+//   P^T = exp2(S^T * scale*log2(e) - m)
+//   O^T += V^T P^T       (A = V^T read with ds_read_b64_tr_b16 from the row-major V tile,
+//                         B = P^T straight from the score registers; K order = accumulator order)
+// The running max m only moves when a row's tile maximum exceeds it by more than 2^8: until then
+// P is computed against the stale m (values up to 256, exact in the float32 sums and harmless in
+// bf16), and O and l are rescaled only on the rare wave-uniform branch where some row moved.
+// L = (m + log2 l) * ln 2 is the natural-log row logsumexp.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ne {
+
+namespace {
+
+constexpr int kTile = 64;     // keys per step
+constexpr int kQBlk = 128;    // queries per workgroup
+constexpr int kThreads = 256;
+constexpr float kRescale = 8.f;   // log2 units of headroom before the running max is moved
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline bf16x4 tr_read(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// A-operand fragment (32 rows m x 16 k) from a row-major LDS tile X[k][m]; see bwd_bf16.hip.
+__device__ inline bf16x8 tr_frag(const bf16* X, int rs, int m0, int kb0, int kb1, int lane) {
+    const int s = lane & 15;
+    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const bf16x4 lo = tr_read(X + (kb0 + (s >> 2)) * rs + m);
+    const bf16x4 hi = tr_read(X + (kb1 + (s >> 2)) * rs + m);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline bf16x2 cvt2(float x, float y) { return __builtin_convertvector(f32x2{x, y}, bf16x2); }
+__device__ inline bf16x4 cvt4(const float* x) {
+    return __builtin_shufflevector(cvt2(x[0], x[1]), cvt2(x[2], x[3]), 0, 1, 2, 3);
+}
+
+__device__ inline float partner_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float partner_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct alignas(16) FwdLds {
+    static constexpr int RS = D + 8;
+    alignas(16) bf16 k[2][kTile * RS];    // K~ tiles [key][d] (rotated)
+    alignas(16) bf16 v[2][kTile * RS];    // V tiles
+};
+
+// Prefetch of one 64-key K/V tile pair (+ the RoPE table rows of its keys).
+template <int D>
+struct KvPrefetch {
+    static constexpr int NU = (kTile * D / 8) / kThreads;
+    static_assert((kTile * D / 8) % kThreads == 0, "tile chunks must cover the workgroup evenly");
+    bf16x8 k[NU], v[NU];
+    f32x4 cs[NU][2];
+
+    __device__ inline void load(const bf16* kb, const bf16* vb, const float* cs_tab, int j0, int T, int tid) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int ch = tid + u * kThreads;
+            const int row = min(j0 + ch / (D / 8), T - 1), d0 = (ch % (D / 8)) * 8;
+            k[u] = *reinterpret_cast<const bf16x8*>(kb + (size_t)row * D + d0);
+            v[u] = *reinterpret_cast<const bf16x8*>(vb + (size_t)row * D + d0);
+            if (cs_tab) {
+                const f32x4* c = reinterpret_cast<const f32x4*>(cs_tab + (size_t)row * D + d0);
+                cs[u][0] = c[0];
+                cs[u][1] = c[1];
+            }
+        }
+    }
+    __device__ inline void store(bf16* sk, bf16* sv, bool rope, int tid) const {
+        constexpr int RS = D + 8;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int ch = tid + u * kThreads;
+            const int o = (ch / (D / 8)) * RS + (ch % (D / 8)) * 8;
+            bf16x8 kk = k[u];
+            if (rope) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (float)kk[e];
+                float y[8];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float c = cs[u][p >> 1][2 * (p & 1)], s = cs[u][p >> 1][2 * (p & 1) + 1];
+                    y[2 * p] = x[2 * p] * c - x[2 * p + 1] * s;
+                    y[2 * p + 1] = x[2 * p] * s + x[2 * p + 1] * c;
+                }
+                kk = __builtin_shufflevector(cvt4(y), cvt4(y + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            *reinterpret_cast<bf16x8*>(sk + o) = kk;
+            *reinterpret_cast<bf16x8*>(sv + o) = v[u];
+        }
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+    using M = Mfma<bf16>;
+    constexpr int NCH = D / 16, NDT = D / 32, RS = FwdLds<D>::RS;
+    __shared__ FwdLds<D> S;
+
+    const int T_ = a.T;
+    const int nqt = (T_ + kQBlk - 1) / kQBlk;
+    const int BH = a.B * a.Hq;
+    const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // most causal work first
+    const int bh = (int)(blockIdx.x % BH);
+    const int b = bh / a.Hq, h = bh % a.Hq;
+    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
+    const int i0 = qt * kQBlk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform across the wave
+    const int col = lane & 31, half = lane >> 5;
+    const int wq0 = i0 + 32 * w;
+    const int qrow = wq0 + col;
+    const float* __restrict__ cs = a.rope_cs;
+    const float c2 = a.scale * kLog2e;
+
+    // this lane's query: rotated, as B operands of S^T = K~ Q~^T
+    bf16x8 qop[NCH];
+    {
+        float x[D / 2];
+        load_row_slots<bf16, D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D,
+                                cs, min(qrow, T_ - 1), half, true, x);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            qop[c] = __builtin_shufflevector(cvt4(x + 8 * c), cvt4(x + 8 * c + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D;
+    const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D;
+    const int kv_end = min(T_, i0 + kQBlk);
+    const int nsteps = (kv_end + kTile - 1) / kTile;
+    KvPrefetch<D> pf;
+    pf.load(kbase, vbase, cs, 0, T_, tid);
+    pf.store(S.k[0], S.v[0], cs != nullptr, tid);
+    __syncthreads();
+
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY;   // reference max, log2 units
+    float l_run = 0.f;         // this lane's share of the row sum (against m_run)
+
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        const int j0 = st * kTile;
+        const bool more = st + 1 < nsteps;
+        if (more) pf.load(kbase, vbase, cs, j0 + kTile, T_, tid);
+        if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
+            const bf16* Ks = S.k[buf];
+            const bf16* Vs = S.v[buf];
+            // all key fragments first, then the two independent accumulation chains interleaved
+            bf16x8 kf[2][NCH];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + col) * RS + 16 * c + 8 * half]);
+            f32x16 sT[2];
+            sT[0] = M::mma(kf[0][0], qop[0], f32x16{});
+            sT[1] = M::mma(kf[1][0], qop[0], f32x16{});
+#pragma unroll
+            for (int c = 1; c < NCH; ++c) {
+                sT[0] = M::mma(kf[0][c], qop[c], sT[0]);
+                sT[1] = M::mma(kf[1][c], qop[c], sT[1]);
+            }
+            if (j0 + kTile - 1 > wq0) {     // diagonal tile for this wave: keys after the query
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (j0 + 32 * kt + acc_row(r, half) > qrow) sT[kt][r] = -INFINITY;
+            }
+            float mx = sT[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sT[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sT[1][r]);
+            mx = partner_max(mx) * c2;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescale) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+                m_run = m_new;
+            }
+            // P^T (B operands, 4 chunks of 16 keys in accumulator order) and the row sum
+            bf16x8 pb[4];
+            float ls = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    float p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[kt][4 * rg + e], c2, -m_run));
+                        ls += p[e];
+                    }
+                    const bf16x4 p4 = cvt4(p);
+                    const int pc = 2 * kt + (rg >> 1);
+                    if (rg & 1) pb[pc] = __builtin_shufflevector(pb[pc].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    else pb[pc] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            l_run += ls;
+            // O^T += V^T P^T  (V^T fragments read first)
+            bf16x8 vf[4][NDT];
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag(Vs, RS, 32 * dt, kb0, kb0 + 8, lane);
+            }
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::mma(vf[pc][dt], pb[pc], oacc[dt]);
+        }
+        if (more) pf.store(S.k[buf ^ 1], S.v[buf ^ 1], cs != nullptr, tid);
+        __syncthreads();
+    }
+
+    // epilogue: O = O^T / l, L = (m + log2 l) ln 2
+    const float l_tot = partner_sum(l_run);
+    if (qrow < T_) {
+        const float inv = 1.f / l_tot;
+        bf16* __restrict__ o = reinterpret_cast<bf16*>(a.o) + ((size_t)bh * T_ + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float x[4] = {oacc[dt][r] * inv, oacc[dt][r + 1] * inv, oacc[dt][r + 2] * inv,
+                                    oacc[dt][r + 3] * inv};
+                *reinterpret_cast<bf16x4*>(o + 32 * dt + acc_row(r, half)) = cvt4(x);
+            }
+        if (half == 0) a.lse[(size_t)bh * T_ + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+}  // namespace
+
+template <int D>
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+    const long blocks = (long)((a.T + kQBlk - 1) / kQBlk) * a.B * a.Hq;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template hipError_t launch_fwd_bf16<64>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_bf16<32>(const FwdArgs&, hipStream_t);
+
+}  // namespace ne

@@ -49,6 +49,7 @@ struct RopeArgs {
 template <typename T, int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
