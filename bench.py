@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the bench, run a plain 256 MiB elementwise copy 5 times (reference kernel of "
+                         "known traffic for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -202,6 +205,15 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.copy_calibration:
+        # a kernel of known traffic: reads 256 MiB and writes 256 MiB per launch
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"kernel": "torch.neg (elementwise)", "read_bytes": src.numel() * 2,
+                                   "write_bytes": dst.numel() * 2, "launches": 5}
     print(json.dumps(out))
 
 

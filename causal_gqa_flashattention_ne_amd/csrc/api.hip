@@ -117,8 +117,8 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
-    // float32: delta | float32 dQ accumulator;  bf16: delta | rotated Q | rotated K (bf16)
-    if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
+    // float32: delta | float32 dQ accumulator;  bf16: delta | rotated Q hi | rotated Q lo | rotated K
+    if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
     return delta_bytes(p) + qe * sizeof(float);
 }
 
@@ -133,14 +133,17 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D;
     float* dq_acc = nullptr;
     void* qrot = nullptr;
+    void* qrot_lo = nullptr;
     void* krot = nullptr;
     if (p->dtype == NE_DTYPE_BF16) {
+        const size_t qb = (qe * 2 + 255) & ~(size_t)255;
         qrot = ws + delta_bytes(p);
-        krot = ws + delta_bytes(p) + ((qe * 2 + 255) & ~(size_t)255);
+        qrot_lo = ws + delta_bytes(p) + qb;
+        krot = ws + delta_bytes(p) + 2 * qb;
     } else {
         dq_acc = reinterpret_cast<float*>(ws + delta_bytes(p));
     }
-    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, qrot, krot, p->rope_cs,
+    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, qrot, qrot_lo, krot, p->rope_cs,
                      p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
     return NE_OK;
 }

@@ -8,8 +8,12 @@
 // the factor enters through the exponent (log2(scale) is folded into L), so dS' feeds dK and dQ
 // directly and dV is divided by scale once at the end.
 //
+// The rotated queries are carried as two bf16 parts, Q~ = hi + lo, in every score product (the
+// forward does the same): S then carries only the rounding of the rotated keys, which keeps the
+// byte-level workload (keys scaled x8) inside the bf16 error bar; Q~^T in the dK product uses hi.
+//
 // Two launches:
-//   bwd_pre_bf16:  delta (float32), Q~ and K~ (bf16, rotated once) into the workspace.
+//   bwd_pre_bf16:  delta (float32), Q~ (hi and lo) and K~ (bf16, rotated once) into the workspace.
 //   bwd_bf16:      one grid, two kinds of workgroups, no atomics and no float32 scratch:
 //     dK/dV blocks (key-tile major): a block owns 64 keys of one (batch, kv head); its 4 waves
 //       split every 64-query step 2 x 2 (wave w: keys 32*(w&1).., queries 32*(w>>1)..), keep
@@ -39,6 +43,7 @@ namespace {
 constexpr int kTile = 64;     // keys per dK/dV block, queries per step; keys per dQ step
 constexpr int kQBlk = 128;    // queries per dQ block
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;      // accelerator complex dies of the MI355X, each with its own L2
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -70,7 +75,8 @@ __device__ inline bf16x4 cvt4(const float* x) {
 template <int D>
 struct alignas(16) DkdvLds {
     static constexpr int RS = D + 8;
-    alignas(16) bf16 q[2][kTile * RS];    // Q~ tiles [query][d]
+    alignas(16) bf16 q[2][kTile * RS];    // Q~ tiles [query][d] (hi part)
+    alignas(16) bf16 ql[2][kTile * RS];   // Q~ remainder tiles (lo part)
     alignas(16) bf16 g[2][kTile * RS];    // dO tiles
     alignas(16) float l[2][kTile];        // L*log2(e) - log2(scale)  (+inf past the sequence end)
     alignas(16) float dl[2][kTile];       // delta
@@ -89,31 +95,31 @@ union alignas(16) BwdLds {
     DqLds<D> q;
 };
 
-// Prefetch of one 64-row x D tile pair: rows clamped into [0, T), loads unconditional, so the
+// Prefetch of NT 64-row x D tiles: rows clamped into [0, T), loads unconditional, so the
 // destination registers are not touched again before the store to LDS.
-template <int D>
-struct TilePair {
+template <int D, int NT>
+struct TileSet {
     static constexpr int NU = (kTile * D / 8) / kThreads;
     static_assert((kTile * D / 8) % kThreads == 0, "tile chunks must cover the workgroup evenly");
-    bf16x8 a[NU], b[NU];
+    bf16x8 x[NT][NU];
 
-    __device__ inline void load(const bf16* pa, const bf16* pb, int last, int tid) {
+    __device__ inline void load(const bf16* const* src, int last, int tid) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int ch = tid + u * kThreads;
             const int off = min(ch / (D / 8), last) * D + (ch % (D / 8)) * 8;
-            a[u] = *reinterpret_cast<const bf16x8*>(pa + off);
-            b[u] = *reinterpret_cast<const bf16x8*>(pb + off);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) x[t][u] = *reinterpret_cast<const bf16x8*>(src[t] + off);
         }
     }
-    __device__ inline void store(bf16* sa, bf16* sb, int tid) const {
+    __device__ inline void store(bf16* const* dst, int tid) const {
         constexpr int RS = D + 8;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int ch = tid + u * kThreads;
             const int o = (ch / (D / 8)) * RS + (ch % (D / 8)) * 8;
-            *reinterpret_cast<bf16x8*>(sa + o) = a[u];
-            *reinterpret_cast<bf16x8*>(sb + o) = b[u];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) *reinterpret_cast<bf16x8*>(dst[t] + o) = x[t][u];
         }
     }
 };
@@ -166,6 +172,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const float sl2 = a.scale * kLog2e;
     const float log2_scale = __log2f(a.scale);
     const bf16* __restrict__ qrot = reinterpret_cast<const bf16*>(a.qrot);
+    const bf16* __restrict__ qrot_lo = reinterpret_cast<const bf16*>(a.qrot_lo);
     const bf16* __restrict__ dout = reinterpret_cast<const bf16*>(a.dout);
 
     // this lane's key row: K~ and V as B operands
@@ -184,17 +191,19 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int nsph = (T_ - j0 + kTile - 1) / kTile;   // query steps per head
     const int nsteps = G * nsph;
     const size_t hrow0 = (size_t)(b * a.Hq + g * G) * T_;
-    TilePair<D> pf;
+    TileSet<D, 3> pf;
     float px = 0.f;
     auto load = [&](int hh, int i0) {
         const size_t hrow = hrow0 + (size_t)hh * T_;
-        pf.load(qrot + (hrow + i0) * D, dout + (hrow + i0) * D, T_ - 1 - i0, tid);
+        const bf16* src[3] = {qrot + (hrow + i0) * D, qrot_lo + (hrow + i0) * D, dout + (hrow + i0) * D};
+        pf.load(src, T_ - 1 - i0, tid);
         const int r = min(tid & (kTile - 1), T_ - 1 - i0);
         if (w == 0) px = a.lse[hrow + i0 + r];
         else if (w == 1) px = a.delta[hrow + i0 + r];
     };
     auto store = [&](int buf, int i0) {
-        pf.store(S.q[buf], S.g[buf], tid);
+        bf16* dst[3] = {S.q[buf], S.ql[buf], S.g[buf]};
+        pf.store(dst, tid);
         const bool in = i0 + (tid & (kTile - 1)) < T_;
         if (w == 0) S.l[buf][tid] = in ? px * kLog2e - log2_scale : INFINITY;
         else if (w == 1) S.dl[buf][tid - kTile] = px;
@@ -218,19 +227,23 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         const bf16* Gs = S.g[buf];
         const bool first = (i0 == j0);
         if (!(first && kh > qh)) {            // blocks wholly above the diagonal are skipped
-            // query / dO fragments first, then the two independent chains interleaved
-            bf16x8 qf[NCH], gf[NCH];
+            // query (hi, lo) / dO fragments first, then the two independent chains interleaved
+            const bf16* Ql = S.ql[buf];
+            bf16x8 qf[NCH], qlf[NCH], gf[NCH];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 qf[c] = *reinterpret_cast<const bf16x8*>(&Qs[(32 * qh + col) * RS + 16 * c + 8 * half]);
+                qlf[c] = *reinterpret_cast<const bf16x8*>(&Ql[(32 * qh + col) * RS + 16 * c + 8 * half]);
                 gf[c] = *reinterpret_cast<const bf16x8*>(&Gs[(32 * qh + col) * RS + 16 * c + 8 * half]);
             }
             f32x16 sacc = M::mma(qf[0], kop[0], f32x16{});
             f32x16 dp = M::mma(gf[0], vop[0], f32x16{});
+            sacc = M::mma(qlf[0], kop[0], sacc);
 #pragma unroll
             for (int c = 1; c < NCH; ++c) {
                 sacc = M::mma(qf[c], kop[c], sacc);
                 dp = M::mma(gf[c], vop[c], dp);
+                sacc = M::mma(qlf[c], kop[c], sacc);
             }
             bf16x8 pb[2], sb[2];
             if (first && kh == qh)
@@ -263,7 +276,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 
     // add the two query halves' partial dK^T / dV^T through LDS (reuses the tile buffers)
     float* red = reinterpret_cast<float*>(&S.q[0][0]);   // [dk|dv][kh][NDT][16 regs][64 lanes]
-    static_assert(sizeof(S.q) + sizeof(S.g) >= 2 * 2 * NDT * 16 * 64 * 4, "reduction buffer too small");
+    static_assert(sizeof(S.q) + sizeof(S.ql) + sizeof(S.g) >= 2 * 2 * NDT * 16 * 64 * 4, "reduction buffer too small");
     if (qh == 1) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -315,14 +328,16 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const size_t qoff = ((size_t)bh * T_ + min(qrow, T_ - 1)) * D;
     const float sl2 = a.scale * kLog2e;
 
-    // this lane's query row: Q~ and dO as B operands, L and delta
-    bf16x8 qop[NCH], gop[NCH];
+    // this lane's query row: Q~ (hi and lo) and dO as B operands, L and delta
+    bf16x8 qop[NCH], qlo[NCH], gop[NCH];
     {
         const bf16* qr = reinterpret_cast<const bf16*>(a.qrot) + qoff + 8 * half;
+        const bf16* ql = reinterpret_cast<const bf16*>(a.qrot_lo) + qoff + 8 * half;
         const bf16* gr = reinterpret_cast<const bf16*>(a.dout) + qoff + 8 * half;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             qop[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+            qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
             gop[c] = *reinterpret_cast<const bf16x8*>(gr + 16 * c);
         }
     }
@@ -334,9 +349,13 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D;
     const int kv_end = min(T_, i0 + kQBlk);
     const int nsteps = (kv_end + kTile - 1) / kTile;
-    TilePair<D> pf;
-    pf.load(kbase, vbase, T_ - 1, tid);
-    pf.store(S.k[0], S.v[0], tid);
+    TileSet<D, 2> pf;
+    {
+        const bf16* src[2] = {kbase, vbase};
+        bf16* dst[2] = {S.k[0], S.v[0]};
+        pf.load(src, T_ - 1, tid);
+        pf.store(dst, tid);
+    }
     __syncthreads();
 
     f32x16 dqt[NDT];
@@ -347,7 +366,10 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         const int buf = st & 1;
         const int j0 = st * kTile;
         const bool more = st + 1 < nsteps;
-        if (more) pf.load(kbase + (size_t)(j0 + kTile) * D, vbase + (size_t)(j0 + kTile) * D, T_ - 1 - j0 - kTile, tid);
+        if (more) {
+            const bf16* src[2] = {kbase + (size_t)(j0 + kTile) * D, vbase + (size_t)(j0 + kTile) * D};
+            pf.load(src, T_ - 1 - j0 - kTile, tid);
+        }
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
@@ -365,6 +387,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             for (int kt = 0; kt < 2; ++kt) {
                 sT[kt] = M::mma(kf[kt][0], qop[0], f32x16{});
                 dpT[kt] = M::mma(vf[kt][0], gop[0], f32x16{});
+                sT[kt] = M::mma(kf[kt][0], qlo[0], sT[kt]);
             }
 #pragma unroll
             for (int c = 1; c < NCH; ++c)
@@ -372,6 +395,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                 for (int kt = 0; kt < 2; ++kt) {
                     sT[kt] = M::mma(kf[kt][c], qop[c], sT[kt]);
                     dpT[kt] = M::mma(vf[kt][c], gop[c], dpT[kt]);
+                    sT[kt] = M::mma(kf[kt][c], qlo[c], sT[kt]);
                 }
             // dS'^T = P' (dP^T - delta), packed as B operands (4 chunks of 16 keys)
             bf16x8 sb[4];
@@ -406,7 +430,10 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
         }
-        if (more) pf.store(S.k[buf ^ 1], S.v[buf ^ 1], tid);
+        if (more) {
+            bf16* dst[2] = {S.k[buf ^ 1], S.v[buf ^ 1]};
+            pf.store(dst, tid);
+        }
         __syncthreads();
     }
 
@@ -428,20 +455,35 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_bf16_kernel(BwdArgs a) {
     __shared__ BwdLds<D> S;
-    const int BG = a.B * a.Hkv, BH = a.B * a.Hq;
-    const int ndk = ((a.T + kTile - 1) / kTile) * BG;
-    const int blk = (int)blockIdx.x;
-    if (blk < ndk) {
-        // key tile 0 has the most causal work: dispatch in increasing key-tile order
-        dkdv_block<D>(a, S.kv, blk / BG, blk % BG);
+    const int BG = a.B * a.Hkv, G = a.Hq / a.Hkv;
+    const int nkv = (a.T + kTile - 1) / kTile;
+    const int nqt = (a.T + kQBlk - 1) / kQBlk;
+    if (BG % kXcds == 0) {
+        // workgroups are dispatched round-robin over the XCDs: block i runs on XCD i % 8.  All
+        // blocks of kv group bg (its dK/dV tiles and the dQ tiles of its query heads) go to XCD
+        // bg % 8, so the group's Q~, dO, K~ and V are fetched into one L2 only.  Within an XCD:
+        // dK/dV blocks first (key tile 0 carries the most causal work), then dQ blocks (last
+        // query tile first).
+        const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+        const int gpx = BG / kXcds;                     // kv groups per XCD
+        if (j < nkv * gpx) {
+            dkdv_block<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
+        } else {
+            const int r = j - nkv * gpx;
+            const int per = gpx * G;
+            const int bg = ((r % per) / G) * kXcds + x;
+            dq_block<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
+        }
     } else {
-        const int r = blk - ndk;
-        const int nqt = (a.T + kQBlk - 1) / kQBlk;
-        dq_block<D>(a, S.q, nqt - 1 - r / BH, r % BH);   // last query tile has the most work
+        const int BH = a.B * a.Hq;
+        const int ndk = nkv * BG;
+        const int blk = (int)blockIdx.x;
+        if (blk < ndk) dkdv_block<D>(a, S.kv, blk / BG, blk % BG);
+        else dq_block<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
     }
 }
 
-// delta_i = sum_d dO_id O_id; Q~ = R q and K~ = R k (bf16) into the workspace.
+// delta_i = sum_d dO_id O_id; Q~ = R q (bf16 hi + lo) and K~ = R k (bf16) into the workspace.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
     constexpr int TPR = D / 8;
@@ -460,7 +502,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum += o[e] * d[e];
         if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, (int)(row % a.T), part * 8, false);
-        store16<bf16>(reinterpret_cast<bf16*>(a.qrot) + off, q);
+        const bf16x8 hi = __builtin_shufflevector(cvt4(q), cvt4(q + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = q[e] - (float)hi[e];
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) =
+            __builtin_shufflevector(cvt4(r), cvt4(r + 4), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int o2 = 1; o2 < TPR; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
         if (part == 0) a.delta[row] = sum;

@@ -9,7 +9,8 @@
 // tile is loaded (clamped, unconditional loads, so nothing waits on them early), the keys are
 // rotated in registers and both tiles stored row-major with 16-byte writes after the current
 // tile's products.  Only tiles at or before the block's last query are visited.
-//   S^T = K~ Q~^T        (A = key rows from LDS, B = this lane's rotated query in registers)
+//   S^T = K~ Q~^T        (A = key rows from LDS, B = this lane's rotated query in registers,
+//                         split into bf16 hi + lo so that only the keys' rounding enters S)
 //   P^T = exp2(S^T * scale*log2(e) - m)
 //   O^T += V^T P^T       (A = V^T read with ds_read_b64_tr_b16 from the row-major V tile,
 //                         B = P^T straight from the score registers; K order = accumulator order)
@@ -28,6 +29,7 @@ constexpr int kTile = 64;     // keys per step
 constexpr int kQBlk = 128;    // queries per workgroup
 constexpr int kThreads = 256;
 constexpr float kRescale = 8.f;   // log2 units of headroom before the running max is moved
+constexpr int kXcds = 8;          // accelerator complex dies of the MI355X, each with its own L2
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -122,11 +124,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     const int T_ = a.T;
     const int nqt = (T_ + kQBlk - 1) / kQBlk;
-    const int BH = a.B * a.Hq;
-    const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // most causal work first
-    const int bh = (int)(blockIdx.x % BH);
-    const int b = bh / a.Hq, h = bh % a.Hq;
-    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
+    const int G = a.Hq / a.Hkv;
+    const int BG = a.B * a.Hkv;
+    int qt, bg, hh;
+    if (BG % kXcds == 0) {
+        // workgroups are dispatched round-robin over the XCDs: block i runs on XCD i % 8.  Every
+        // query head of kv group bg is placed on XCD bg % 8, so the group's K/V tiles are fetched
+        // into one L2 only; within an XCD the blocks run most causal work first.
+        const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+        const int per = (BG / kXcds) * G;               // blocks of one query tile on one XCD
+        qt = nqt - 1 - j / per;
+        bg = ((j % per) / G) * kXcds + x;
+        hh = (j % per) % G;
+    } else {
+        const int BH = a.B * a.Hq;
+        qt = nqt - 1 - (int)(blockIdx.x / BH);          // most causal work first
+        const int bhh = (int)(blockIdx.x % BH);
+        bg = bhh / G;
+        hh = bhh % G;
+    }
+    const int bh = bg * G + hh;                         // = b * Hq + h
     const int i0 = qt * kQBlk;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform across the wave
@@ -136,15 +153,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     const float* __restrict__ cs = a.rope_cs;
     const float c2 = a.scale * kLog2e;
 
-    // this lane's query: rotated, as B operands of S^T = K~ Q~^T
-    bf16x8 qop[NCH];
+    // this lane's query, rotated in float32 and held as two bf16 B operands (hi + lo) of
+    // S^T = K~ Q~^T: the rotated query is then exact to ~2^-16 in the score product, and only the
+    // rounding of the rotated keys remains (the dominant bf16 error once keys are large)
+    bf16x8 qhi[NCH], qlo[NCH];
     {
         float x[D / 2];
         load_row_slots<bf16, D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D,
                                 cs, min(qrow, T_ - 1), half, true, x);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            qop[c] = __builtin_shufflevector(cvt4(x + 8 * c), cvt4(x + 8 * c + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int c = 0; c < NCH; ++c) {
+            qhi[c] = __builtin_shufflevector(cvt4(x + 8 * c), cvt4(x + 8 * c + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+            float r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = x[8 * c + e] - (float)qhi[c][e];
+            qlo[c] = __builtin_shufflevector(cvt4(r), cvt4(r + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
     }
 
     const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D;
@@ -178,12 +202,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                 for (int c = 0; c < NCH; ++c)
                     kf[kt][c] = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + col) * RS + 16 * c + 8 * half]);
             f32x16 sT[2];
-            sT[0] = M::mma(kf[0][0], qop[0], f32x16{});
-            sT[1] = M::mma(kf[1][0], qop[0], f32x16{});
+            sT[0] = M::mma(kf[0][0], qhi[0], f32x16{});
+            sT[1] = M::mma(kf[1][0], qhi[0], f32x16{});
+            sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
+            sT[1] = M::mma(kf[1][0], qlo[0], sT[1]);
 #pragma unroll
             for (int c = 1; c < NCH; ++c) {
-                sT[0] = M::mma(kf[0][c], qop[c], sT[0]);
-                sT[1] = M::mma(kf[1][c], qop[c], sT[1]);
+                sT[0] = M::mma(kf[0][c], qhi[c], sT[0]);
+                sT[1] = M::mma(kf[1][c], qhi[c], sT[1]);
+                sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
+                sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
             }
             if (j0 + kTile - 1 > wq0) {     // diagonal tile for this wave: keys after the query
 #pragma unroll

@@ -29,7 +29,8 @@ struct BwdArgs {
     void* dv;
     float* delta;           // workspace: [B, Hq, T] rowsum(dO * O)
     float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
-    void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q, written by the preprocess
+    void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q rounded to bf16 (hi part)
+    void* qrot_lo;          // workspace (bf16 path): [B, Hq, T, D] bf16 remainder, rotated Q = hi + lo
     void* krot;             // workspace (bf16 path): [B, Hkv, T, D] rotated K, written by the preprocess
     const float* rope_cs;
     int B, Hq, Hkv, T;

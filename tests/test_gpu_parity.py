@@ -1,9 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the double-precision oracle.
 
 Small shapes span several tiles and ragged tails and are checked element by element in full.
-The five workloads run at their full sizes in the benchmark's launch configuration; where the
-oracle would be slow, it is evaluated on sampled (batch, kv group) units, each of which is an
-independent piece of the computation (every query head of the group, all positions).
+The five workloads run at their full sizes in the benchmark's launch configuration and their whole
+output tensors are compared (every kv group), since the bar is relative to the scale of the whole
+tensor.
 """
 import sys
 
@@ -54,16 +54,12 @@ def test_workload_full_f32(cfg):
         check(q, k, v, do, w.dtype, theta=w.theta, label="%s layer %d" % (w.name, layer))
 
 
-@pytest.mark.parametrize("cfg,layers,groups", [
-    (3, [0], [(0, 0), (7, 2), (15, 3)]),
-    (4, [0, 15], [(3, 1), (12, 0)]),
-    (5, [0], [(0, 0), (5, 6)]),
-])
-def test_workload_full_size_sampled(cfg, layers, groups):
+@pytest.mark.parametrize("cfg,layers", [(3, [0]), (4, [0, 15]), (5, [0])])
+def test_workload_full_size(cfg, layers):
+    """Whole output tensors at the full workload size against the oracle (every kv group)."""
     w = gen.WORKLOADS[cfg]
     for layer in layers:
-        log("workload %d layer %d groups %s" % (cfg, layer, groups))
+        log("workload %d layer %d (all groups)" % (cfg, layer))
         q, k, v, do = gen.layer_inputs(w, layer)
-        errs = check(q, k, v, do, w.dtype, theta=w.theta, groups=groups,
-                     label="%s layer %d" % (w.name, layer))
+        errs = check(q, k, v, do, w.dtype, theta=w.theta, label="%s layer %d" % (w.name, layer))
         log("  errors %s" % errs)
