@@ -50,6 +50,21 @@ def kernel_bytes(w, elem):
     }
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter profile of this workload, or None
+    when there is none or the kernel sources changed since it was taken."""
+    from causal_gqa_flashattention_ne_amd import profsum
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != profsum.source_hash() or kernel not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel]
+    return k["read_bytes"] + k["write_bytes"]
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -154,7 +169,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": kbytes[dom] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, dom)
     roof["kernel"] = dom
     roof["avg_us"] = avg_us[dom]
     roof["algorithmic_flop"] = kflops[dom]

@@ -1,11 +1,60 @@
-"""Summarise a rocprofv3 kernel trace (rocpd SQLite database or kernel_stats CSV) per kernel.
+"""Summaries of rocprofv3 output.
 
     python -m causal_gqa_flashattention_ne_amd.profsum <results.db | kernel_stats.csv>
-Prints one line per kernel: dispatch count, average / min / max duration in microseconds.
+        one line per kernel: dispatch count, average / min / max duration in microseconds.
+    python -m causal_gqa_flashattention_ne_amd.profsum traffic <FETCH_SIZE dir> <WRITE_SIZE dir> <out.json>
+        per-kernel HBM bytes per dispatch from two counter runs (--pmc FETCH_SIZE, then
+        --pmc WRITE_SIZE) of `bench.py --copy-calibration`, each scaled by what the same counter
+        reads for the calibration copy (256 MiB read + 256 MiB written per launch), tagged with a
+        hash of the kernel sources so that the benchmark stops quoting it once a kernel changes.
 """
+import collections
 import csv
+import glob
+import hashlib
+import json
+import os
 import sqlite3
 import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNELS = {"fwd_bf16_kernel": "fwd", "bwd_pre_bf16_kernel": "bwd_pre", "bwd_bf16_kernel": "bwd_main",
+           "fwd_kernel": "fwd", "bwd_pre_kernel": "bwd_pre", "bwd_main_kernel": "bwd_main"}
+CAL_BYTES = 256 << 20
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def counter_avgs(d):
+    vals = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)   # KiB -> bytes
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def traffic(fetch_dir, write_dir, out):
+    fetch, write = counter_avgs(fetch_dir), counter_avgs(write_dir)
+    cal = [k for k in fetch if "neg_kernel" in k]
+    if not cal:
+        raise SystemExit("no calibration copy kernel in %s" % fetch_dir)
+    rf = CAL_BYTES / fetch[cal[0]]
+    wf = CAL_BYTES / write[cal[0]]
+    res = {"source_sha256": source_hash(), "read_scale": rf, "write_scale": wf, "kernels": {}}
+    for name in fetch:
+        for key, short in KERNELS.items():
+            if key + "<" in name or name.endswith(key) or ("::" + key + "(") in name:
+                res["kernels"][short] = {"name": name, "read_bytes": fetch[name] * rf,
+                                         "write_bytes": write.get(name, 0.0) * wf}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
 
 
 def rows_from_db(path):
@@ -32,4 +81,7 @@ def main(path):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1])
+    if sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4])
+    else:
+        main(sys.argv[1])
