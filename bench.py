@@ -114,7 +114,7 @@ def main():
             ne.attn_fwd_into(p, q, k, v, o, lse, st)
             if ev is not None:
                 ev[1][li].record(stream)
-            ne.attn_bwd_preprocess_into(p, q, k, o, do, ws, st)
+            ne.attn_bwd_preprocess_into(p, q, k, o, lse, do, ws, st)
             if ev is not None:
                 ev[2][li].record(stream)
             ne.attn_bwd_main_into(p, q, k, v, lse, do, dq, dk, dv, ws, st)

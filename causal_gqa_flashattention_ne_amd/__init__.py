@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd",
            "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main")
@@ -73,7 +73,7 @@ def lib():
         L.ne_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnParams)]
         L.ne_attn_bwd_workspace_bytes.restype = sz
         L.ne_attn_bwd.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
-        L.ne_attn_bwd_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, sz, vp]
+        L.ne_attn_bwd_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         L.ne_attn_bwd_main.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 8 + [vp, sz, vp]
         for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
                   "ne_attn_bwd_main"):
@@ -175,11 +175,11 @@ def attn_bwd_into(p: AttnParams, q, k, v, o, lse, do, dq, dk, dv, ws, stream=Non
                                             ws.numel() * ws.element_size(), st))
 
 
-def attn_bwd_preprocess_into(p: AttnParams, q, k, o, do, ws, stream=None):
+def attn_bwd_preprocess_into(p: AttnParams, q, k, o, lse, do, ws, stream=None):
     st = stream if stream is not None else _stream(o.device)
     _check("ne_attn_bwd_preprocess", lib().ne_attn_bwd_preprocess(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(o),
-                                                                  _ptr(do), _ptr(ws), ws.numel() * ws.element_size(),
-                                                                  st))
+                                                                  _ptr(lse), _ptr(do), _ptr(ws),
+                                                                  ws.numel() * ws.element_size(), st))
 
 
 def attn_bwd_main_into(p: AttnParams, q, k, v, lse, do, dq, dk, dv, ws, stream=None):

@@ -43,8 +43,13 @@ int check_ptrs(std::initializer_list<const void*> ps) {
     return NE_OK;
 }
 
+int padded_rows(int T) { return (T + 63) / 64 * 64; }
+
+// per-row float32 data: float32 path delta [B, Hq, T]; bf16 path (l', delta) pairs for every row of
+// whole 64-row tiles
 size_t delta_bytes(const ne_attn_params* p) {
-    size_t n = (size_t)p->B * p->Hq * p->T * sizeof(float);
+    size_t n = p->dtype == NE_DTYPE_BF16 ? (size_t)p->B * p->Hq * padded_rows(p->T) * 2 * sizeof(float)
+                                         : (size_t)p->B * p->Hq * p->T * sizeof(float);
     return (n + 255) & ~(size_t)255;
 }
 
@@ -117,7 +122,8 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
-    // float32: delta | float32 dQ accumulator;  bf16: delta | rotated Q hi | rotated Q lo | rotated K
+    // float32: delta | float32 dQ accumulator
+    // bf16: (l', delta) per row | rotated Q hi | rotated Q lo | rotated K
     if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
     return delta_bytes(p) + qe * sizeof(float);
 }
@@ -129,32 +135,36 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
     if (int rc = check_attn(p)) return rc;
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    float* delta = reinterpret_cast<float*>(ws);
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D;
+    float* delta = nullptr;
+    float* ld = nullptr;
     float* dq_acc = nullptr;
     void* qrot = nullptr;
     void* qrot_lo = nullptr;
     void* krot = nullptr;
     if (p->dtype == NE_DTYPE_BF16) {
         const size_t qb = (qe * 2 + 255) & ~(size_t)255;
+        ld = reinterpret_cast<float*>(ws);
         qrot = ws + delta_bytes(p);
         qrot_lo = ws + delta_bytes(p) + qb;
         krot = ws + delta_bytes(p) + 2 * qb;
     } else {
+        delta = reinterpret_cast<float*>(ws);
         dq_acc = reinterpret_cast<float*>(ws + delta_bytes(p));
     }
-    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, dq_acc, qrot, qrot_lo, krot, p->rope_cs,
-                     p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
+    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, qrot, qrot_lo, krot, p->rope_cs,
+                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p)};
     return NE_OK;
 }
 }  // namespace
 
 int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k, const void* o,
-                           const void* dout, void* workspace, size_t workspace_bytes, void* stream) {
+                           const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     if (int rc = check_attn(p)) return rc;
-    if (int rc = check_ptrs({q, k, o, dout, workspace})) return rc;
+    if (int rc = check_ptrs({q, k, o, lse, dout, workspace})) return rc;
     ne::BwdArgs a;
-    if (int rc = bwd_args(p, q, k, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+    if (int rc = bwd_args(p, q, k, nullptr, o, lse, dout, nullptr, nullptr, nullptr,
                           workspace, workspace_bytes, &a)) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
@@ -191,7 +201,7 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
     if (int rc = check_attn(p)) return rc;
     if (int rc = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return rc;
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    if (int rc = ne_attn_bwd_preprocess(p, q, k, o, dout, workspace, workspace_bytes, stream)) return rc;
+    if (int rc = ne_attn_bwd_preprocess(p, q, k, o, lse, dout, workspace, workspace_bytes, stream)) return rc;
     return ne_attn_bwd_main(p, q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 

@@ -5,15 +5,17 @@
 //     S = Q~ K~^T, P = exp(scale*S - L), dP = dO V^T, dS = P * (dP - delta),
 //     dV = P^T dO,  dK = R^T (scale * dS^T Q~),  dQ = R^T (scale * dS K~),
 // where delta_i = sum_d dO_id O_id.  The kernels work with P' = scale * P and dS' = scale * dS:
-// the factor enters through the exponent (log2(scale) is folded into L), so dS' feeds dK and dQ
-// directly and dV is divided by scale once at the end.
+// the factor enters through the exponent (l' = L log2(e) - log2(scale) is what the kernels
+// subtract), so dS' feeds dK and dQ directly and dV is divided by scale once at the end.
 //
 // The rotated queries are carried as two bf16 parts, Q~ = hi + lo, in every score product (the
 // forward does the same): S then carries only the rounding of the rotated keys, which keeps the
 // byte-level workload (keys scaled x8) inside the bf16 error bar; Q~^T in the dK product uses hi.
 //
 // Two launches:
-//   bwd_pre_bf16:  delta (float32), Q~ (hi and lo) and K~ (bf16, rotated once) into the workspace.
+//   bwd_pre_bf16:  per query row delta and l' (float32, padded per head to whole 64-row tiles:
+//     +inf / 0 past the sequence end, so padded rows get P = 0), Q~ (hi and lo) and K~ (bf16,
+//     rotated once), all into the workspace.
 //   bwd_bf16:      one grid, two kinds of workgroups, no atomics and no float32 scratch:
 //     dK/dV blocks (key-tile major): a block owns 64 keys of one (batch, kv head); its 4 waves
 //       split every 64-query step 2 x 2 (wave w: keys 32*(w&1).., queries 32*(w>>1)..), keep
@@ -26,67 +28,141 @@
 //       queries 32w..32w+31, one lane per query.  Key/value tiles of 64 stream through LDS;
 //       S^T = K~ Q~^T and dP^T = V dO^T put one query per lane, and dQ^T += K~^T dS'^T takes
 //       dS'^T straight from the registers.  dQ is un-rotated and written once.
-//   Tiles are double-buffered in LDS; the next tile is loaded from global memory (clamped,
-//   unconditional loads) while the current one is used.  Every LDS tile is row-major, written
-//   with 16-byte stores; transposed operands come from ds_read_b64_tr_b16, which transposes
-//   16-bit elements across each 16-lane group.  Blocks are ordered heaviest causal work first;
-//   tiles wholly above the diagonal are never visited.  The two roles recompute S and dP
-//   separately (7 products per score instead of 5) in exchange for having no cross-XCD
-//   float32 atomics, which on this machine go out to the memory fabric.
+//   Tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no registers, no
+//   LDS store instructions, per-lane offsets fixed for the whole loop) through three stages, two steps ahead of their use; each step opens
+//   with a wait for this wave's copies of the current tile and one barrier.  LDS tiles are
+//   unpadded and XOR-swizzled in 16-byte chunks (see Swz) so that row reads (ds_read_b128) and
+//   transposed reads (ds_read_b64_tr_b16) stay conflict-free.  Blocks are ordered heaviest
+//   causal work first; tiles wholly above the diagonal are never visited.  The two roles
+//   recompute S and dP separately in exchange for having no cross-XCD float32 atomics, which on
+//   this machine go out to the memory fabric.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace ne {
 
 namespace {
 
-constexpr int kTile = 64;     // keys per dK/dV block, queries per step; keys per dQ step
-constexpr int kQBlk = 128;    // queries per dQ block
-constexpr int kThreads = 256;
-constexpr int kXcds = 8;      // accelerator complex dies of the MI355X, each with its own L2
+constexpr int kTile = kTileRows;       // keys per dK/dV block, queries per step; keys per dQ step
+constexpr int kQBlk = 128;             // queries per dQ block
+constexpr int kThreads = kBlockThreads;
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
+constexpr int kStages = 3;             // LDS stages: a tile is fetched two steps before its use
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element (i % 4) of the 8-byte
-// rows read by lanes (i / 4) + 4k, k = 0..3.
-__device__ inline bf16x4 tr_read(const bf16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+// Unpadded LDS tile of 64 rows x D bf16.  The 16-byte chunk c of row r is stored at chunk
+// position c ^ f(r): any 8 consecutive rows then put a given column chunk in 8 different bank
+// groups, and the 4-row x 32-byte footprint of a transposed read is spread as well.
+template <int D>
+struct Swz {
+    static constexpr int CPR = D / 8;                                  // chunks per row
+    __device__ static inline int f(int r) { return (r * CPR / 8) & (CPR - 1); }
+    // element offset of (row r, column col); a read of up to 8 elements starting at col must not
+    // cross a chunk boundary
+    __device__ static inline int at(int r, int col) { return r * D + (((col >> 3) ^ f(r)) << 3) + (col & 7); }
+};
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them)
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A-operand fragment (32 rows m x 16 k) of the 32x32x16 MFMA taken from a row-major LDS tile
-// X[k][m] (so A[m][k] = X[k][m]): lane (m = l%32, half h) receives X[k][m] for the k rows
-// kb0 + 0..3 and kb1 + 0..3 (kb0 / kb1 chosen per half by the caller).  rs = row stride.
-__device__ inline bf16x8 tr_frag(const bf16* X, int rs, int m0, int kb0, int kb1, int lane) {
+// Barrier between the waves of the workgroup without a memory fence (the fence of
+// __syncthreads would also wait for the copies still in flight); the empty asm keeps the
+// compiler from moving LDS accesses across it.
+__device__ inline void step_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (gfx9 family): base address, stride 0, size in bytes (reads at or past it
+// return zeros), 32-bit data format.  All fields are wave-uniform.
+__device__ inline i32x4 buffer_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long adr = reinterpret_cast<unsigned long long>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)adr);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(adr >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a __shared__ object (taken once per block; per-step addresses are offsets
+// from it in scalar registers).
+__device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(lds_void*)p; }
+
+// One 16-byte-per-lane copy from a buffer into LDS (buffer_load_dwordx4 ... lds): lane i reads at
+// byte voff + soff of the buffer and writes bytes 16i..16i+15 after the wave-uniform LDS byte
+// address lds.  Written as assembly so that the compiler does not track these copies: its
+// automatic wait before a transposed LDS read would otherwise also wait for the copies of the
+// tiles two steps ahead.  Every wait on them is the explicit wait_vmcnt at the top of a step; the
+// per-lane operands loaded before a step loop are waited for (vmcnt(0)) before the loop starts, so
+// no other vector-memory load is in flight in it.
+__device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+
+// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles.  Each wave
+// issues D / 32 copies of 64 lanes x 16 bytes; the LDS side of one copy is a contiguous 1 KiB
+// slice, so the swizzle is applied by choosing which chunk each lane fetches.  The per-lane byte
+// offsets within a tile do not depend on the tile; rows past the end of the buffer read as zeros.
+template <int D>
+struct TileCopy {
+    static constexpr int CPR = D / 8, NU = kTile * CPR / (64 * kWaves);
+    static_assert(NU >= 1 && (kTile * CPR) % (64 * kWaves) == 0, "tile chunks must cover the waves evenly");
+    static constexpr unsigned kBytes = kTile * D * 2;   // one LDS tile
+    unsigned voff[NU];
+    __device__ inline void init(int w, int lane) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = (u * kWaves + w) * 64 + lane;
+            const int r = idx / CPR, p = idx % CPR;
+            voff[u] = (unsigned)(r * D + ((p ^ Swz<D>::f(r)) << 3)) * 2u;
+        }
+    }
+    // the tile whose first row starts at byte row0 of the buffer, into the LDS tile at byte lds
+    __device__ inline void copy(i32x4 rsrc, unsigned row0, unsigned lds, int w) const {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) copy16_to_lds(rsrc, voff[u], row0, lds + (unsigned)(u * kWaves + w) * 1024u);
+    }
+};
+
+// (l', delta) of a 64-row query tile, stored in the workspace exactly as in LDS: 4 groups of 16
+// rows [l' x 16 | delta x 16] (512 bytes per tile); wave w copies group w with 8 lanes.
+__device__ inline int ld_lsc(int q) { return (q >> 4) * 32 + (q & 15); }
+__device__ inline int ld_dlt(int q) { return (q >> 4) * 32 + 16 + (q & 15); }
+
+// Transposed A-operand fragment from a swizzled tile; see tr_frag (tiles.hpp) for the lane map.
+template <int D>
+__device__ inline bf16x8 tr_frag_swz(const bf16* X, int m0, int kb0, int kb1, int lane) {
     const int s = lane & 15;
     const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const bf16x4 lo = tr_read(X + (kb0 + (s >> 2)) * rs + m);
-    const bf16x4 hi = tr_read(X + (kb1 + (s >> 2)) * rs + m);
+    const bf16x4 lo = tr_read(X + Swz<D>::at(kb0 + (s >> 2), m));
+    const bf16x4 hi = tr_read(X + Swz<D>::at(kb1 + (s >> 2), m));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
-__device__ inline bf16x2 cvt2(float x, float y) { return __builtin_convertvector(f32x2{x, y}, bf16x2); }
-
-__device__ inline bf16x4 cvt4(const float* x) {
-    return __builtin_shufflevector(cvt2(x[0], x[1]), cvt2(x[2], x[3]), 0, 1, 2, 3);
 }
 
 template <int D>
 struct alignas(16) DkdvLds {
-    static constexpr int RS = D + 8;
-    alignas(16) bf16 q[2][kTile * RS];    // Q~ tiles [query][d] (hi part)
-    alignas(16) bf16 ql[2][kTile * RS];   // Q~ remainder tiles (lo part)
-    alignas(16) bf16 g[2][kTile * RS];    // dO tiles
-    alignas(16) float l[2][kTile];        // L*log2(e) - log2(scale)  (+inf past the sequence end)
-    alignas(16) float dl[2][kTile];       // delta
+    alignas(16) bf16 q[kStages][kTile * D];    // Q~ tiles [query][d] (hi part)
+    alignas(16) bf16 ql[kStages][kTile * D];   // Q~ remainder tiles (lo part)
+    alignas(16) bf16 g[kStages][kTile * D];    // dO tiles
+    alignas(16) float ld[kStages][2 * kTile];  // l' and delta, see ld_lsc
 };
 
 template <int D>
 struct alignas(16) DqLds {
-    static constexpr int RS = D + 8;
-    alignas(16) bf16 k[2][kTile * RS];    // K~ tiles [key][d]
-    alignas(16) bf16 v[2][kTile * RS];    // V tiles
+    alignas(16) bf16 k[kStages][kTile * D];    // K~ tiles [key][d]
+    alignas(16) bf16 v[kStages][kTile * D];    // V tiles
 };
 
 template <int D>
@@ -95,45 +171,16 @@ union alignas(16) BwdLds {
     DqLds<D> q;
 };
 
-// Prefetch of NT 64-row x D tiles: rows clamped into [0, T), loads unconditional, so the
-// destination registers are not touched again before the store to LDS.
-template <int D, int NT>
-struct TileSet {
-    static constexpr int NU = (kTile * D / 8) / kThreads;
-    static_assert((kTile * D / 8) % kThreads == 0, "tile chunks must cover the workgroup evenly");
-    bf16x8 x[NT][NU];
-
-    __device__ inline void load(const bf16* const* src, int last, int tid) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kThreads;
-            const int off = min(ch / (D / 8), last) * D + (ch % (D / 8)) * 8;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) x[t][u] = *reinterpret_cast<const bf16x8*>(src[t] + off);
-        }
-    }
-    __device__ inline void store(bf16* const* dst, int tid) const {
-        constexpr int RS = D + 8;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kThreads;
-            const int o = (ch / (D / 8)) * RS + (ch % (D / 8)) * 8;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) *reinterpret_cast<bf16x8*>(dst[t] + o) = x[t][u];
-        }
-    }
-};
-
 // One 32 x 32 dK/dV block: P' and dS' for this wave's keys (lane) and queries (registers),
 // packed to bf16 as B operands of the dV / dK products.
 template <bool MASKED>
-__device__ inline void kv_softmax(const f32x16& s, const f32x16& dp, const float* lsc, const float* dl,
-                                  float sl2, int kloc, int qbase, int half, bf16x8* pb, bf16x8* sb) {
+__device__ inline void kv_softmax(const f32x16& s, const f32x16& dp, const float* ld, float sl2, int kloc,
+                                  int qbase, int half, bf16x8* pb, bf16x8* sb) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
         const int q0 = qbase + 8 * rg + 4 * half;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsc + q0);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(dl + q0);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(ld + ld_lsc(q0));
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(ld + ld_dlt(q0));
         float p[4], d[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -158,7 +205,8 @@ __device__ inline void kv_softmax(const f32x16& s, const f32x16& dp, const float
 template <int D>
 __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     using M = Mfma<bf16>;
-    constexpr int NCH = D / 16, NDT = D / 32, RS = DkdvLds<D>::RS;
+    constexpr int NCH = D / 16, NDT = D / 32;
+    constexpr int kCopies = 3 * TileCopy<D>::NU + 1;   // copies per wave per step: 3 tiles + l'/delta
     const int T_ = a.T;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.Hq / a.Hkv;
@@ -170,10 +218,41 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int kloc = 32 * kh + col;
     const int key = j0 + kloc;
     const float sl2 = a.scale * kLog2e;
-    const float log2_scale = __log2f(a.scale);
     const bf16* __restrict__ qrot = reinterpret_cast<const bf16*>(a.qrot);
     const bf16* __restrict__ qrot_lo = reinterpret_cast<const bf16*>(a.qrot_lo);
     const bf16* __restrict__ dout = reinterpret_cast<const bf16*>(a.dout);
+
+    const int nsph = (T_ - j0 + kTile - 1) / kTile;   // query steps per head
+    const int nsteps = G * nsph;
+    const int hq0 = b * a.Hq + g * G;                 // first query head of the group
+    const int ntile = a.Tp / kTile;                   // (l', delta) tiles per head
+    // buffers over the group's query heads; step st covers query tile jt + st % nsph of head
+    // hq0 + st / nsph (tile rows past T read another head's rows or zeros: l' = +inf there)
+    const size_t hoff = (size_t)hq0 * T_ * D;
+    const unsigned gbytes = (unsigned)(G * T_) * (unsigned)(D * 2);   // < 2^32: at most 2^31 - 1 elements
+    const i32x4 rq = buffer_rsrc(qrot + hoff, gbytes);
+    const i32x4 rql = buffer_rsrc(qrot_lo + hoff, gbytes);
+    const i32x4 rg = buffer_rsrc(dout + hoff, gbytes);
+    const i32x4 rld = buffer_rsrc(a.ld + (size_t)hq0 * ntile * 2 * kTile, (unsigned)(G * ntile) * (unsigned)(2 * kTile * 4));
+    const unsigned lq = lds_addr(&S.q[0][0]), lql = lds_addr(&S.ql[0][0]), lg = lds_addr(&S.g[0][0]);
+    const unsigned lld = lds_addr(&S.ld[0][0]);
+    TileCopy<D> tc;
+    tc.init(w, lane);
+    auto issue = [&](int hh, int t, int buf) {
+        const unsigned row0 = (unsigned)(hh * T_ + j0 + t * kTile) * (unsigned)(D * 2);
+        const unsigned so = (unsigned)buf * TileCopy<D>::kBytes;
+        tc.copy(rq, row0, lq + so, w);
+        tc.copy(rql, row0, lql + so, w);
+        tc.copy(rg, row0, lg + so, w);
+        if (lane < 8)
+            copy16_to_lds(rld, (unsigned)(w * 128 + lane * 16), (unsigned)(hh * ntile + jt + t) * 512u,
+                          lld + (unsigned)(buf * 512 + w * 128));
+    };
+    issue(0, 0, 0);
+    int ih = 0, it = 1;                               // head / tile of the next step to issue
+    if (it == nsph) { it = 0; ++ih; }
+    if (nsteps > 1) issue(ih, it, 1);
+    if (++it == nsph) { it = 0; ++ih; }
 
     // this lane's key row: K~ and V as B operands
     bf16x8 kop[NCH], vop[NCH];
@@ -187,55 +266,45 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
             vop[c] = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
         }
     }
+    wait_vmcnt<0>();   // operands and the first two tiles (see copy16_to_lds)
 
-    const int nsph = (T_ - j0 + kTile - 1) / kTile;   // query steps per head
-    const int nsteps = G * nsph;
-    const size_t hrow0 = (size_t)(b * a.Hq + g * G) * T_;
-    TileSet<D, 3> pf;
-    float px = 0.f;
-    auto load = [&](int hh, int i0) {
-        const size_t hrow = hrow0 + (size_t)hh * T_;
-        const bf16* src[3] = {qrot + (hrow + i0) * D, qrot_lo + (hrow + i0) * D, dout + (hrow + i0) * D};
-        pf.load(src, T_ - 1 - i0, tid);
-        const int r = min(tid & (kTile - 1), T_ - 1 - i0);
-        if (w == 0) px = a.lse[hrow + i0 + r];
-        else if (w == 1) px = a.delta[hrow + i0 + r];
-    };
-    auto store = [&](int buf, int i0) {
-        bf16* dst[3] = {S.q[buf], S.ql[buf], S.g[buf]};
-        pf.store(dst, tid);
-        const bool in = i0 + (tid & (kTile - 1)) < T_;
-        if (w == 0) S.l[buf][tid] = in ? px * kLog2e - log2_scale : INFINITY;
-        else if (w == 1) S.dl[buf][tid - kTile] = px;
-    };
-    load(0, j0);
-    store(0, j0);
-    __syncthreads();
+    // per-lane LDS offsets of the row fragments (query row 32*qh + col, chunks 2c + half)
+    int roff[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) roff[c] = Swz<D>::at(32 * qh + col, 16 * c + 8 * half);
 
     f32x16 dkt[NDT], dvt[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) { dkt[i] = f32x16{}; dvt[i] = f32x16{}; }
 
-    int hh = 0, i0 = j0;
+    int buf = 0, ct = 0;                              // stage and query tile of the current step
     for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        int nhh = hh, ni0 = i0 + kTile;
-        if (ni0 >= T_) { ni0 = j0; ++nhh; }
-        const bool more = st + 1 < nsteps;
-        if (more) load(nhh, ni0);
+        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
+        else wait_vmcnt<0>();
+        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
+        if (st + 2 < nsteps) {
+            issue(ih, it, buf == 0 ? 2 : buf - 1);
+            if (++it == nsph) { it = 0; ++ih; }
+        }
         const bf16* Qs = S.q[buf];
+        const bf16* Ql = S.ql[buf];
         const bf16* Gs = S.g[buf];
-        const bool first = (i0 == j0);
+        const float* Ld = S.ld[buf];
+        const bool first = ct == 0;
         if (!(first && kh > qh)) {            // blocks wholly above the diagonal are skipped
-            // query (hi, lo) / dO fragments first, then the two independent chains interleaved
-            const bf16* Ql = S.ql[buf];
+            // All LDS reads of a product are issued together ahead of it (sched_barrier keeps the
+            // scheduler from sinking them next to their uses, which would expose the LDS latency
+            // on every MFMA): row fragments, then S / dP; the transposed fragments of the dV / dK
+            // products are read while the softmax waits for S and dP.
             bf16x8 qf[NCH], qlf[NCH], gf[NCH];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                qf[c] = *reinterpret_cast<const bf16x8*>(&Qs[(32 * qh + col) * RS + 16 * c + 8 * half]);
-                qlf[c] = *reinterpret_cast<const bf16x8*>(&Ql[(32 * qh + col) * RS + 16 * c + 8 * half]);
-                gf[c] = *reinterpret_cast<const bf16x8*>(&Gs[(32 * qh + col) * RS + 16 * c + 8 * half]);
+                qf[c] = *reinterpret_cast<const bf16x8*>(Qs + roff[c]);
+                qlf[c] = *reinterpret_cast<const bf16x8*>(Ql + roff[c]);
+                gf[c] = *reinterpret_cast<const bf16x8*>(Gs + roff[c]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
             f32x16 sacc = M::mma(qf[0], kop[0], f32x16{});
             f32x16 dp = M::mma(gf[0], vop[0], f32x16{});
             sacc = M::mma(qlf[0], kop[0], sacc);
@@ -245,21 +314,26 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                 dp = M::mma(gf[c], vop[c], dp);
                 sacc = M::mma(qlf[c], kop[c], sacc);
             }
-            bf16x8 pb[2], sb[2];
-            if (first && kh == qh)
-                kv_softmax<true>(sacc, dp, S.l[buf], S.dl[buf], sl2, kloc, 32 * qh, half, pb, sb);
-            else
-                kv_softmax<false>(sacc, dp, S.l[buf], S.dl[buf], sl2, kloc, 32 * qh, half, pb, sb);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
             bf16x8 gt[2][NDT], qtf[2][NDT];
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 const int kb0 = 32 * qh + 16 * pc + 4 * half;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    gt[pc][dt] = tr_frag(Gs, RS, 32 * dt, kb0, kb0 + 8, lane);
-                    qtf[pc][dt] = tr_frag(Qs, RS, 32 * dt, kb0, kb0 + 8, lane);
+                    gt[pc][dt] = tr_frag_swz<D>(Gs, 32 * dt, kb0, kb0 + 8, lane);
+                    qtf[pc][dt] = tr_frag_swz<D>(Qs, 32 * dt, kb0, kb0 + 8, lane);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 pb[2], sb[2];
+            if (first && kh == qh)
+                kv_softmax<true>(sacc, dp, Ld, sl2, kloc, 32 * qh, half, pb, sb);
+            else
+                kv_softmax<false>(sacc, dp, Ld, sl2, kloc, 32 * qh, half, pb, sb);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
@@ -267,14 +341,15 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                     dvt[dt] = M::mma(gt[pc][dt], pb[pc], dvt[dt]);
                     dkt[dt] = M::mma(qtf[pc][dt], sb[pc], dkt[dt]);
                 }
+            __builtin_amdgcn_s_setprio(0);
         }
-        if (more) store(buf ^ 1, ni0);
-        __syncthreads();
-        hh = nhh;
-        i0 = ni0;
+        buf = buf == kStages - 1 ? 0 : buf + 1;
+        if (++ct == nsph) ct = 0;
     }
 
-    // add the two query halves' partial dK^T / dV^T through LDS (reuses the tile buffers)
+    // add the two query halves' partial dK^T / dV^T through LDS (reuses the tile buffers once
+    // every wave is past its last step)
+    __syncthreads();
     float* red = reinterpret_cast<float*>(&S.q[0][0]);   // [dk|dv][kh][NDT][16 regs][64 lanes]
     static_assert(sizeof(S.q) + sizeof(S.ql) + sizeof(S.g) >= 2 * 2 * NDT * 16 * 64 * 4, "reduction buffer too small");
     if (qh == 1) {
@@ -289,6 +364,9 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     __syncthreads();
     if (qh == 0 && key < T_) {
         const float inv_scale = 1.f / a.scale;     // dV was accumulated from P' = scale * P
+        const bool rope = a.rope_cs != nullptr;
+        f32x4 cs[NDT][4];
+        if (rope) load_acc_cs<D>(a.rope_cs, key, half, cs);
         const size_t base = ((size_t)bg * T_ + key) * D;
         bf16* __restrict__ dk = reinterpret_cast<bf16*>(a.dk) + base;
         bf16* __restrict__ dv = reinterpret_cast<bf16*>(a.dv) + base;
@@ -303,7 +381,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                     y[e] = (dvt[dt][r + e] + red[(((2 + kh) * NDT + dt) * 16 + r + e) * 64 + lane]) * inv_scale;
                 }
                 const int d = 32 * dt + acc_row(r, half);
-                if (a.rope_cs) rope_rotate(x, 4, a.rope_cs, D, key, d, true);
+                if (rope) unrotate4(x, cs[dt][r / 4]);
                 *reinterpret_cast<bf16x4*>(dk + d) = cvt4(x);
                 *reinterpret_cast<bf16x4*>(dv + d) = cvt4(y);
             }
@@ -315,7 +393,8 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 template <int D>
 __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     using M = Mfma<bf16>;
-    constexpr int NCH = D / 16, NDT = D / 32, RS = DqLds<D>::RS;
+    constexpr int NCH = D / 16, NDT = D / 32;
+    constexpr int kCopies = 2 * TileCopy<D>::NU;     // copies per wave per step: K~ and V tiles
     const int T_ = a.T;
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
@@ -328,7 +407,24 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const size_t qoff = ((size_t)bh * T_ + min(qrow, T_ - 1)) * D;
     const float sl2 = a.scale * kLog2e;
 
-    // this lane's query row: Q~ (hi and lo) and dO as B operands, L and delta
+    const int kv_end = min(T_, i0 + kQBlk);
+    const int nsteps = (kv_end + kTile - 1) / kTile;
+    // buffers over kv head bg (key rows past T read as zeros; they are causally masked)
+    const unsigned hbytes = (unsigned)T_ * (unsigned)(D * 2);
+    const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.krot) + (size_t)bg * T_ * D, hbytes);
+    const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D, hbytes);
+    const unsigned lk = lds_addr(&S.k[0][0]), lv = lds_addr(&S.v[0][0]);
+    TileCopy<D> tc;
+    tc.init(w, lane);
+    auto issue = [&](int st, int buf) {
+        const unsigned row0 = (unsigned)(st * kTile) * (unsigned)(D * 2), so = (unsigned)buf * TileCopy<D>::kBytes;
+        tc.copy(rk, row0, lk + so, w);
+        tc.copy(rv, row0, lv + so, w);
+    };
+    issue(0, 0);
+    if (nsteps > 1) issue(1, 1);
+
+    // this lane's query row: Q~ (hi and lo) and dO as B operands, l' and delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
     {
         const bf16* qr = reinterpret_cast<const bf16*>(a.qrot) + qoff + 8 * half;
@@ -341,47 +437,45 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             gop[c] = *reinterpret_cast<const bf16x8*>(gr + 16 * c);
         }
     }
-    const size_t rowi = (size_t)bh * T_ + min(qrow, T_ - 1);
-    const float lsc = a.lse[rowi] * kLog2e - __log2f(a.scale);
-    const float dlt = a.delta[rowi];
+    const int rowc = min(qrow, T_ - 1);
+    const float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + rowc / kTile) * 2 * kTile;
+    const float lsc = ldt[ld_lsc(rowc % kTile)];
+    const float dlt = ldt[ld_dlt(rowc % kTile)];
+    wait_vmcnt<0>();   // operands and the first two tiles (see copy16_to_lds)
 
-    const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.krot) + (size_t)bg * T_ * D;
-    const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D;
-    const int kv_end = min(T_, i0 + kQBlk);
-    const int nsteps = (kv_end + kTile - 1) / kTile;
-    TileSet<D, 2> pf;
-    {
-        const bf16* src[2] = {kbase, vbase};
-        bf16* dst[2] = {S.k[0], S.v[0]};
-        pf.load(src, T_ - 1, tid);
-        pf.store(dst, tid);
-    }
-    __syncthreads();
+    // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
+    int roff[2][NCH];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) roff[kt][c] = Swz<D>::at(32 * kt + col, 16 * c + 8 * half);
 
     f32x16 dqt[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) dqt[i] = f32x16{};
 
+    int buf = 0;                                      // stage of the current step
     for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
+        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
+        else wait_vmcnt<0>();
+        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
+        if (st + 2 < nsteps) issue(st + 2, buf == 0 ? 2 : buf - 1);
         const int j0 = st * kTile;
-        const bool more = st + 1 < nsteps;
-        if (more) {
-            const bf16* src[2] = {kbase + (size_t)(j0 + kTile) * D, vbase + (size_t)(j0 + kTile) * D};
-            pf.load(src, T_ - 1 - j0 - kTile, tid);
-        }
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
-            // key / value fragments first, then four independent chains interleaved
+            // key / value row fragments as one batch, then four independent chains interleaved;
+            // the transposed K~ fragments of the dQ product are read while the softmax waits
             bf16x8 kf[2][NCH], vf[2][NCH];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + col) * RS + 16 * c + 8 * half]);
-                    vf[kt][c] = *reinterpret_cast<const bf16x8*>(&Vs[(32 * kt + col) * RS + 16 * c + 8 * half]);
+                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(Ks + roff[kt][c]);
+                    vf[kt][c] = *reinterpret_cast<const bf16x8*>(Vs + roff[kt][c]);
                 }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
             f32x16 sT[2], dpT[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
@@ -397,6 +491,16 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                     dpT[kt] = M::mma(vf[kt][c], gop[c], dpT[kt]);
                     sT[kt] = M::mma(kf[kt][c], qlo[c], sT[kt]);
                 }
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 ktf[4][NDT];
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_swz<D>(Ks, 32 * dt, kb0, kb0 + 8, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // dS'^T = P' (dP^T - delta), packed as B operands (4 chunks of 16 keys)
             bf16x8 sb[4];
             const bool diag = j0 + kTile - 1 > wq0;
@@ -418,27 +522,22 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                     else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             // dQ~^T (D x 32 queries) += K~^T dS'^T  (K = the tile's keys, accumulator order)
-            bf16x8 ktf[4][NDT];
-#pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag(Ks, RS, 32 * dt, kb0, kb0 + 8, lane);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
+            __builtin_amdgcn_s_setprio(0);
         }
-        if (more) {
-            bf16* dst[2] = {S.k[buf ^ 1], S.v[buf ^ 1]};
-            pf.store(dst, tid);
-        }
-        __syncthreads();
+        buf = buf == kStages - 1 ? 0 : buf + 1;
     }
 
     // dQ = R^T dQ~ ; lane owns one query, 4 consecutive d per register group
     if (qrow < T_) {
+        const bool rope = a.rope_cs != nullptr;
+        f32x4 cs[NDT][4];
+        if (rope) load_acc_cs<D>(a.rope_cs, qrow, half, cs);
         bf16* __restrict__ dq = reinterpret_cast<bf16*>(a.dq) + ((size_t)bh * T_ + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -446,7 +545,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             for (int r = 0; r < 16; r += 4) {
                 float x[4] = {dqt[dt][r], dqt[dt][r + 1], dqt[dt][r + 2], dqt[dt][r + 3]};
                 const int d = 32 * dt + acc_row(r, half);
-                if (a.rope_cs) rope_rotate(x, 4, a.rope_cs, D, qrow, d, true);
+                if (rope) unrotate4(x, cs[dt][r / 4]);
                 *reinterpret_cast<bf16x4*>(dq + d) = cvt4(x);
             }
     }
@@ -483,35 +582,42 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_bf16_kernel(BwdArgs a) {
     }
 }
 
-// delta_i = sum_d dO_id O_id; Q~ = R q (bf16 hi + lo) and K~ = R k (bf16) into the workspace.
+// Per query row (padded per head to Tp rows): delta = sum_d dO O and l' = L log2(e) -
+// log2(scale) (rows past T: 0 and +inf) into the tile layout of ld_lsc; Q~ = R q as bf16 hi + lo;
+// then K~ = R k (bf16).
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
     constexpr int TPR = D / 8;
-    const long qrows = (long)a.B * a.Hq * a.T;
+    const long qrows = (long)a.B * a.Hq * a.Tp;
     const long krows = (long)a.B * a.Hkv * a.T;
     const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
     const long row = gid / TPR;
     const int part = (int)(gid % TPR);
     if (row < qrows) {
-        const size_t off = (size_t)row * D + part * 8;
-        float o[8], d[8], q[8];
-        load16<bf16>(reinterpret_cast<const bf16*>(a.o) + off, o);
-        load16<bf16>(reinterpret_cast<const bf16*>(a.dout) + off, d);
-        load16<bf16>(reinterpret_cast<const bf16*>(a.q) + off, q);
+        const long bh = row / a.Tp;
+        const int t = (int)(row % a.Tp);
         float sum = 0.f;
+        if (t < a.T) {
+            const size_t off = ((size_t)bh * a.T + t) * D + part * 8;
+            float o[8], d[8], q[8];
+            load16<bf16>(reinterpret_cast<const bf16*>(a.o) + off, o);
+            load16<bf16>(reinterpret_cast<const bf16*>(a.dout) + off, d);
+            load16<bf16>(reinterpret_cast<const bf16*>(a.q) + off, q);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += o[e] * d[e];
-        if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, (int)(row % a.T), part * 8, false);
-        const bf16x8 hi = __builtin_shufflevector(cvt4(q), cvt4(q + 4), 0, 1, 2, 3, 4, 5, 6, 7);
-        float r[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = q[e] - (float)hi[e];
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) =
-            __builtin_shufflevector(cvt4(r), cvt4(r + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int e = 0; e < 8; ++e) sum += o[e] * d[e];
+            if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, t, part * 8, false);
+            const bf16x8 hi = cvt8(q);
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) = remainder8(q, hi);
+        }
 #pragma unroll
         for (int o2 = 1; o2 < TPR; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
-        if (part == 0) a.delta[row] = sum;
+        if (part == 0) {
+            float* ldt = a.ld + (row / kTile) * 2 * kTile;   // rows of a head are whole tiles (Tp)
+            const int r = t % kTile;
+            ldt[ld_lsc(r)] = t < a.T ? a.lse[bh * a.T + t] * kLog2e - __log2f(a.scale) : INFINITY;
+            ldt[ld_dlt(r)] = sum;
+        }
     } else if (row < qrows + krows) {
         const long kr = row - qrows;
         const size_t off = (size_t)kr * D + part * 8;
@@ -526,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream) {
-    const long rows = (long)a.B * (a.Hq + a.Hkv) * a.T;
+    const long rows = (long)a.B * a.Hq * a.Tp + (long)a.B * a.Hkv * a.T;
     const long threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, a);

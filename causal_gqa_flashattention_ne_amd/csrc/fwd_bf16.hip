@@ -20,37 +20,17 @@
 // L = (m + log2 l) * ln 2 is the natural-log row logsumexp.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace ne {
 
 namespace {
 
-constexpr int kTile = 64;     // keys per step
-constexpr int kQBlk = 128;    // queries per workgroup
-constexpr int kThreads = 256;
-constexpr float kRescale = 8.f;   // log2 units of headroom before the running max is moved
-constexpr int kXcds = 8;          // accelerator complex dies of the MI355X, each with its own L2
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ inline bf16x4 tr_read(const bf16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-// A-operand fragment (32 rows m x 16 k) from a row-major LDS tile X[k][m]; see bwd_bf16.hip.
-__device__ inline bf16x8 tr_frag(const bf16* X, int rs, int m0, int kb0, int kb1, int lane) {
-    const int s = lane & 15;
-    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const bf16x4 lo = tr_read(X + (kb0 + (s >> 2)) * rs + m);
-    const bf16x4 hi = tr_read(X + (kb1 + (s >> 2)) * rs + m);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ inline bf16x2 cvt2(float x, float y) { return __builtin_convertvector(f32x2{x, y}, bf16x2); }
-__device__ inline bf16x4 cvt4(const float* x) {
-    return __builtin_shufflevector(cvt2(x[0], x[1]), cvt2(x[2], x[3]), 0, 1, 2, 3);
-}
+constexpr int kTile = kTileRows;       // keys per step
+constexpr int kQBlk = 128;             // queries per workgroup
+constexpr int kThreads = kBlockThreads;
+constexpr float kRescale = 8.f;        // log2 units of headroom before the running max is moved
+constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
 
 __device__ inline float partner_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -66,54 +46,6 @@ struct alignas(16) FwdLds {
     static constexpr int RS = D + 8;
     alignas(16) bf16 k[2][kTile * RS];    // K~ tiles [key][d] (rotated)
     alignas(16) bf16 v[2][kTile * RS];    // V tiles
-};
-
-// Prefetch of one 64-key K/V tile pair (+ the RoPE table rows of its keys).
-template <int D>
-struct KvPrefetch {
-    static constexpr int NU = (kTile * D / 8) / kThreads;
-    static_assert((kTile * D / 8) % kThreads == 0, "tile chunks must cover the workgroup evenly");
-    bf16x8 k[NU], v[NU];
-    f32x4 cs[NU][2];
-
-    __device__ inline void load(const bf16* kb, const bf16* vb, const float* cs_tab, int j0, int T, int tid) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kThreads;
-            const int row = min(j0 + ch / (D / 8), T - 1), d0 = (ch % (D / 8)) * 8;
-            k[u] = *reinterpret_cast<const bf16x8*>(kb + (size_t)row * D + d0);
-            v[u] = *reinterpret_cast<const bf16x8*>(vb + (size_t)row * D + d0);
-            if (cs_tab) {
-                const f32x4* c = reinterpret_cast<const f32x4*>(cs_tab + (size_t)row * D + d0);
-                cs[u][0] = c[0];
-                cs[u][1] = c[1];
-            }
-        }
-    }
-    __device__ inline void store(bf16* sk, bf16* sv, bool rope, int tid) const {
-        constexpr int RS = D + 8;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kThreads;
-            const int o = (ch / (D / 8)) * RS + (ch % (D / 8)) * 8;
-            bf16x8 kk = k[u];
-            if (rope) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (float)kk[e];
-                float y[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float c = cs[u][p >> 1][2 * (p & 1)], s = cs[u][p >> 1][2 * (p & 1) + 1];
-                    y[2 * p] = x[2 * p] * c - x[2 * p + 1] * s;
-                    y[2 * p + 1] = x[2 * p] * s + x[2 * p + 1] * c;
-                }
-                kk = __builtin_shufflevector(cvt4(y), cvt4(y + 4), 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            *reinterpret_cast<bf16x8*>(sk + o) = kk;
-            *reinterpret_cast<bf16x8*>(sv + o) = v[u];
-        }
-    }
 };
 
 template <int D>
@@ -157,27 +89,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     // S^T = K~ Q~^T: the rotated query is then exact to ~2^-16 in the score product, and only the
     // rounding of the rotated keys remains (the dominant bf16 error once keys are large)
     bf16x8 qhi[NCH], qlo[NCH];
-    {
-        float x[D / 2];
-        load_row_slots<bf16, D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D,
-                                cs, min(qrow, T_ - 1), half, true, x);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            qhi[c] = __builtin_shufflevector(cvt4(x + 8 * c), cvt4(x + 8 * c + 4), 0, 1, 2, 3, 4, 5, 6, 7);
-            float r[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r[e] = x[8 * c + e] - (float)qhi[c][e];
-            qlo[c] = __builtin_shufflevector(cvt4(r), cvt4(r + 4), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    }
+    row_operands<D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D, cs,
+                    min(qrow, T_ - 1), half, qhi, qlo);
 
     const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D;
     const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D;
     const int kv_end = min(T_, i0 + kQBlk);
     const int nsteps = (kv_end + kTile - 1) / kTile;
-    KvPrefetch<D> pf;
-    pf.load(kbase, vbase, cs, 0, T_, tid);
-    pf.store(S.k[0], S.v[0], cs != nullptr, tid);
+    TileLoad<D, 2, false> pf;
+    {
+        const bf16* src[2] = {kbase, vbase};
+        bf16* dst[2] = {S.k[0], S.v[0]};
+        pf.load(src, cs, 0, T_ - 1, tid);
+        pf.store(dst, cs != nullptr, tid);
+    }
     __syncthreads();
 
     f32x16 oacc[NDT];
@@ -190,7 +115,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         const int buf = st & 1;
         const int j0 = st * kTile;
         const bool more = st + 1 < nsteps;
-        if (more) pf.load(kbase, vbase, cs, j0 + kTile, T_, tid);
+        if (more) {
+            const bf16* src[2] = {kbase + (size_t)(j0 + kTile) * D, vbase + (size_t)(j0 + kTile) * D};
+            pf.load(src, cs, j0 + kTile, T_ - 1 - j0 - kTile, tid);
+        }
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
@@ -266,7 +194,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::mma(vf[pc][dt], pb[pc], oacc[dt]);
         }
-        if (more) pf.store(S.k[buf ^ 1], S.v[buf ^ 1], cs != nullptr, tid);
+        if (more) {
+            bf16* dst[2] = {S.k[buf ^ 1], S.v[buf ^ 1]};
+            pf.store(dst, cs != nullptr, tid);
+        }
         __syncthreads();
     }
 

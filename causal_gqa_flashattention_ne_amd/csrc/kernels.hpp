@@ -27,13 +27,16 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;           // workspace: [B, Hq, T] rowsum(dO * O)
+    float* delta;           // workspace (float32 path): [B, Hq, T] rowsum(dO * O)
+    float* ld;              // workspace (bf16 path): per query head and 64-row tile, 4 groups of
+                            // [l' x 16 | delta x 16] (l' = L log2(e) - log2(scale); rows >= T: +inf, 0)
     float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
     void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q rounded to bf16 (hi part)
     void* qrot_lo;          // workspace (bf16 path): [B, Hq, T, D] bf16 remainder, rotated Q = hi + lo
     void* krot;             // workspace (bf16 path): [B, Hkv, T, D] rotated K, written by the preprocess
     const float* rope_cs;
     int B, Hq, Hkv, T;
+    int Tp;                 // T rounded up to whole 64-row tiles
     float scale;
 };
 

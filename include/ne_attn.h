@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 1
+#define NE_ABI_VERSION 2
 
 enum {
     NE_OK = 0,
@@ -127,13 +127,15 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
  * ne_attn_bwd_preprocess: delta_i = sum_d dout_id * o_id (float32) for every query row, the
  * per-row term of the softmax backward dS = P * (dP - delta), written into the workspace, which
  * it also prepares for ne_attn_bwd_main (float32: a zeroed dQ accumulator; bf16: the rotated
- * queries R q and keys R k).  Reads q, k, o and dout; writes only the workspace.
+ * queries R q and keys R k and, from lse, the per-row exponent offset).  Reads q, k, o, lse and
+ * dout; writes only the workspace.
  *
  * ne_attn_bwd_main: dq, dk, dv as ne_attn_bwd, from a workspace that ne_attn_bwd_preprocess filled
  * for the same parameters, o and dout (stream order), with no call on that workspace in between.
  */
 int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k, const void* o,
-                           const void* dout, void* workspace, size_t workspace_bytes, void* stream);
+                           const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
+                           void* stream);
 int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, const void* v,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream);

@@ -105,8 +105,10 @@ def test_workspace_size_and_check():
     p = params(B=2, Hq=4, Hkv=2, T=16, D=64)
     need = ne.bwd_workspace_bytes(p)
     delta = 2 * 4 * 16 * 4
-    # bf16: delta | rotated Q hi | rotated Q lo | rotated K;  float32: delta | float32 dQ accumulator
-    assert need == ((delta + 255) // 256) * 256 + 2 * (2 * 4 * 16 * 64 * 2) + 2 * 2 * 16 * 64 * 2
+    rows_padded = 2 * 4 * 64         # bf16: rows of each head padded to whole 64-row tiles
+    # bf16: (l', delta) per padded row | rotated Q hi | rotated Q lo | rotated K
+    # float32: delta | float32 dQ accumulator
+    assert need == rows_padded * 2 * 4 + 2 * (2 * 4 * 16 * 64 * 2) + 2 * 2 * 16 * 64 * 2
     pf = params(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_F32)
     assert ne.bwd_workspace_bytes(pf) == ((delta + 255) // 256) * 256 + 2 * 4 * 16 * 64 * 4
     assert bwd(p, ws_bytes=need - 1) == -5
