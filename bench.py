@@ -100,6 +100,7 @@ def main():
     cs = ne.rope_table(w.T, w.D, w.theta, dev)
     p = ne.make_params(w.B, w.Hq, w.Hkv, w.T, w.D, ne._dtype_code(layers[0][0]), None, cs)
     ws = torch.empty(ne.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, ne.fwd_workspace_bytes(p)), dtype=torch.uint8, device=dev)
     outs = []
     for (q, k, v, do) in layers:
         outs.append((torch.empty_like(q), torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev),
@@ -111,7 +112,7 @@ def main():
         for li, ((q, k, v, do), (o, lse, dq, dk, dv)) in enumerate(zip(layers, outs)):
             if ev is not None:
                 ev[0][li].record(stream)
-            ne.attn_fwd_into(p, q, k, v, o, lse, st)
+            ne.attn_fwd_into(p, q, k, v, o, lse, fws, st)
             if ev is not None:
                 ev[1][li].record(stream)
             ne.attn_bwd_preprocess_into(p, q, k, o, lse, do, ws, st)

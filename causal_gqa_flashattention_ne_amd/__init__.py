@@ -27,10 +27,10 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
-EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd",
-           "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main")
+EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
+           "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main")
 
 
 class AttnParams(ctypes.Structure):
@@ -69,7 +69,9 @@ def lib():
         L.ne_status_string.restype = ctypes.c_char_p
         L.ne_rope_table.argtypes = [i32, i32, ctypes.c_double, vp, vp]
         L.ne_rope_apply.argtypes = [ctypes.POINTER(RopeParams), vp, vp, ctypes.c_int, vp]
-        L.ne_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp]
+        L.ne_attn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnParams)]
+        L.ne_attn_fwd_workspace_bytes.restype = sz
+        L.ne_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         L.ne_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnParams)]
         L.ne_attn_bwd_workspace_bytes.restype = sz
         L.ne_attn_bwd.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
@@ -161,10 +163,16 @@ def _params_for(q, k, rope_theta, scale):
     return make_params(B, Hq, Hkv, T, D, _dtype_code(q), scale, cs), cs
 
 
-def attn_fwd_into(p: AttnParams, q, k, v, o, lse, stream=None):
-    """Forward into preallocated o/lse (no allocation, no checks beyond the library's)."""
+def attn_fwd_into(p: AttnParams, q, k, v, o, lse, ws=None, stream=None):
+    """Forward into preallocated o/lse with the workspace tensor ws (uint8; allocated here when None
+    and fwd_workspace_bytes(p) > 0).  No checks beyond the library's."""
     st = stream if stream is not None else _stream(q.device)
-    _check("ne_attn_fwd", lib().ne_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), st))
+    if ws is None:
+        n = fwd_workspace_bytes(p)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    wp, wn = (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+    _check("ne_attn_fwd", lib().ne_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            wp, wn, st))
 
 
 def attn_bwd_into(p: AttnParams, q, k, v, o, lse, do, dq, dk, dv, ws, stream=None):
@@ -187,6 +195,10 @@ def attn_bwd_main_into(p: AttnParams, q, k, v, lse, do, dq, dk, dv, ws, stream=N
     _check("ne_attn_bwd_main", lib().ne_attn_bwd_main(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse),
                                                       _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                                       ws.numel() * ws.element_size(), st))
+
+
+def fwd_workspace_bytes(p: AttnParams) -> int:
+    return int(lib().ne_attn_fwd_workspace_bytes(ctypes.byref(p)))
 
 
 def bwd_workspace_bytes(p: AttnParams) -> int:

@@ -105,17 +105,39 @@ int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, 
     });
 }
 
+size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p) {
+    if (check_attn(p) != NE_OK) return 0;
+    // bf16 with RoPE: the rotated keys, written once and read by every query head of their group
+    if (p->dtype == NE_DTYPE_BF16 && p->rope_cs) return (size_t)p->B * p->Hkv * p->T * p->D * 2;
+    return 0;
+}
+
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
-                float* lse, void* stream) {
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     if (int rc = check_attn(p)) return rc;
     if (int rc = check_ptrs({q, k, v, o, lse})) return rc;
-    ne::FwdArgs a{q, k, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
+    const size_t need = ne_attn_fwd_workspace_bytes(p);
+    if (need) {
+        if (!workspace) return NE_ERR_NULL;
+        if (!aligned16(workspace)) return NE_ERR_ALIGN;
+        if (workspace_bytes < need) return NE_ERR_WORKSPACE;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    ne::FwdArgs a{q, k, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p)};
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
-        if constexpr (std::is_same<T, ne::bf16>::value) return ne::launch_fwd_bf16<DD>(a, s);
-        else return ne::launch_fwd<T, DD>(a, s);
+        if constexpr (std::is_same<T, ne::bf16>::value) {
+            if (need) {
+                ne::RopeArgs r{k, workspace, p->rope_cs, p->B * p->Hkv * p->T, p->T, 0, 0};
+                const hipError_t e = ne::launch_rope<T, DD>(r, s);
+                if (e != hipSuccess) return e;
+                a.k = workspace;
+            }
+            return ne::launch_fwd_bf16<DD>(a, s);
+        } else {
+            return ne::launch_fwd<T, DD>(a, s);
+        }
     });
 }
 

@@ -28,12 +28,9 @@
 //       queries 32w..32w+31, one lane per query.  Key/value tiles of 64 stream through LDS;
 //       S^T = K~ Q~^T and dP^T = V dO^T put one query per lane, and dQ^T += K~^T dS'^T takes
 //       dS'^T straight from the registers.  dQ is un-rotated and written once.
-//   Tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no registers, no
-//   LDS store instructions, per-lane offsets fixed for the whole loop) through three stages, two steps ahead of their use; each step opens
-//   with a wait for this wave's copies of the current tile and one barrier.  LDS tiles are
-//   unpadded and XOR-swizzled in 16-byte chunks (see Swz) so that row reads (ds_read_b128) and
-//   transposed reads (ds_read_b64_tr_b16) stay conflict-free.  Blocks are ordered heaviest
-//   causal work first; tiles wholly above the diagonal are never visited.  The two roles
+//   Tiles reach LDS through the three-stage copy pipeline of tiles.hpp (buffer_load ... lds two
+//   steps ahead, swizzled unpadded tiles, one wait and one barrier per step).  Blocks are ordered
+//   heaviest causal work first; tiles wholly above the diagonal are never visited.  The two roles
 //   recompute S and dP separately in exchange for having no cross-XCD float32 atomics, which on
 //   this machine go out to the memory fabric.
 #include "common.hpp"
@@ -47,109 +44,13 @@ namespace {
 constexpr int kTile = kTileRows;       // keys per dK/dV block, queries per step; keys per dQ step
 constexpr int kQBlk = 128;             // queries per dQ block
 constexpr int kThreads = kBlockThreads;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = kBlockWaves;
 constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
-constexpr int kStages = 3;             // LDS stages: a tile is fetched two steps before its use
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Unpadded LDS tile of 64 rows x D bf16.  The 16-byte chunk c of row r is stored at chunk
-// position c ^ f(r): any 8 consecutive rows then put a given column chunk in 8 different bank
-// groups, and the 4-row x 32-byte footprint of a transposed read is spread as well.
-template <int D>
-struct Swz {
-    static constexpr int CPR = D / 8;                                  // chunks per row
-    __device__ static inline int f(int r) { return (r * CPR / 8) & (CPR - 1); }
-    // element offset of (row r, column col); a read of up to 8 elements starting at col must not
-    // cross a chunk boundary
-    __device__ static inline int at(int r, int col) { return r * D + (((col >> 3) ^ f(r)) << 3) + (col & 7); }
-};
-
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them)
-template <int N>
-__device__ inline void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Barrier between the waves of the workgroup without a memory fence (the fence of
-// __syncthreads would also wait for the copies still in flight); the empty asm keeps the
-// compiler from moving LDS accesses across it.
-__device__ inline void step_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (gfx9 family): base address, stride 0, size in bytes (reads at or past it
-// return zeros), 32-bit data format.  All fields are wave-uniform.
-__device__ inline i32x4 buffer_rsrc(const void* base, unsigned bytes) {
-    const unsigned long long adr = reinterpret_cast<unsigned long long>(base);
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)adr);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(adr >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// LDS byte address of a __shared__ object (taken once per block; per-step addresses are offsets
-// from it in scalar registers).
-__device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(lds_void*)p; }
-
-// One 16-byte-per-lane copy from a buffer into LDS (buffer_load_dwordx4 ... lds): lane i reads at
-// byte voff + soff of the buffer and writes bytes 16i..16i+15 after the wave-uniform LDS byte
-// address lds.  Written as assembly so that the compiler does not track these copies: its
-// automatic wait before a transposed LDS read would otherwise also wait for the copies of the
-// tiles two steps ahead.  Every wait on them is the explicit wait_vmcnt at the top of a step; the
-// per-lane operands loaded before a step loop are waited for (vmcnt(0)) before the loop starts, so
-// no other vector-memory load is in flight in it.
-__device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
-                 : "memory");
-}
-
-// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles.  Each wave
-// issues D / 32 copies of 64 lanes x 16 bytes; the LDS side of one copy is a contiguous 1 KiB
-// slice, so the swizzle is applied by choosing which chunk each lane fetches.  The per-lane byte
-// offsets within a tile do not depend on the tile; rows past the end of the buffer read as zeros.
-template <int D>
-struct TileCopy {
-    static constexpr int CPR = D / 8, NU = kTile * CPR / (64 * kWaves);
-    static_assert(NU >= 1 && (kTile * CPR) % (64 * kWaves) == 0, "tile chunks must cover the waves evenly");
-    static constexpr unsigned kBytes = kTile * D * 2;   // one LDS tile
-    unsigned voff[NU];
-    __device__ inline void init(int w, int lane) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int idx = (u * kWaves + w) * 64 + lane;
-            const int r = idx / CPR, p = idx % CPR;
-            voff[u] = (unsigned)(r * D + ((p ^ Swz<D>::f(r)) << 3)) * 2u;
-        }
-    }
-    // the tile whose first row starts at byte row0 of the buffer, into the LDS tile at byte lds
-    __device__ inline void copy(i32x4 rsrc, unsigned row0, unsigned lds, int w) const {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) copy16_to_lds(rsrc, voff[u], row0, lds + (unsigned)(u * kWaves + w) * 1024u);
-    }
-};
 
 // (l', delta) of a 64-row query tile, stored in the workspace exactly as in LDS: 4 groups of 16
 // rows [l' x 16 | delta x 16] (512 bytes per tile); wave w copies group w with 8 lanes.
 __device__ inline int ld_lsc(int q) { return (q >> 4) * 32 + (q & 15); }
 __device__ inline int ld_dlt(int q) { return (q >> 4) * 32 + 16 + (q & 15); }
-
-// Transposed A-operand fragment from a swizzled tile; see tr_frag (tiles.hpp) for the lane map.
-template <int D>
-__device__ inline bf16x8 tr_frag_swz(const bf16* X, int m0, int kb0, int kb1, int lane) {
-    const int s = lane & 15;
-    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const bf16x4 lo = tr_read(X + Swz<D>::at(kb0 + (s >> 2), m));
-    const bf16x4 hi = tr_read(X + Swz<D>::at(kb1 + (s >> 2), m));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 template <int D>
 struct alignas(16) DkdvLds {

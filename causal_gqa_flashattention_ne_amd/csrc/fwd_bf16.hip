@@ -1,14 +1,14 @@
 // fwd_bf16.hip -- bf16 causal GQA FlashAttention forward for gfx950 (float32 path: fwd.hip).
 //
 // Tiling plus an online softmax, so the T x T matrix is never stored (agentlenshq NanoEuler page,
-// section "커널 구현"); RoPE is applied to queries and keys as they are loaded (same page,
-// "기술 사양").
+// section "커널 구현"); RoPE is applied to the queries as they are loaded and to the keys once
+// per call (same page, "기술 사양").
 //
 // A workgroup owns 128 queries of one (batch, query head); wave w owns queries 32w..32w+31,
-// one lane per query.  Key/value tiles of 64 rows stream through LDS, double-buffered: the next
-// tile is loaded (clamped, unconditional loads, so nothing waits on them early), the keys are
-// rotated in registers and both tiles stored row-major with 16-byte writes after the current
-// tile's products.  Only tiles at or before the block's last query are visited.
+// one lane per query.  The keys arrive already rotated (K~ = R k, written once per call by the
+// RoPE kernel, so no query head of a group rotates them again).  Key/value tiles of 64 rows reach
+// LDS through the three-stage copy pipeline of tiles.hpp (buffer_load ... lds two steps ahead of
+// use, swizzled unpadded tiles).  Only tiles at or before the block's last query are visited.
 //   S^T = K~ Q~^T        (A = key rows from LDS, B = this lane's rotated query in registers,
 //                         split into bf16 hi + lo so that only the keys' rounding enters S)
 //   P^T = exp2(S^T * scale*log2(e) - m)
@@ -43,15 +43,15 @@ __device__ inline float partner_sum(float x) {
 
 template <int D>
 struct alignas(16) FwdLds {
-    static constexpr int RS = D + 8;
-    alignas(16) bf16 k[2][kTile * RS];    // K~ tiles [key][d] (rotated)
-    alignas(16) bf16 v[2][kTile * RS];    // V tiles
+    alignas(16) bf16 k[kStages][kTile * D];    // K~ tiles [key][d] (swizzled)
+    alignas(16) bf16 v[kStages][kTile * D];    // V tiles
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     using M = Mfma<bf16>;
-    constexpr int NCH = D / 16, NDT = D / 32, RS = FwdLds<D>::RS;
+    constexpr int NCH = D / 16, NDT = D / 32;
+    constexpr int kCopies = 2 * TileCopy<D>::NU;      // copies per wave per step: K~ and V tiles
     __shared__ FwdLds<D> S;
 
     const int T_ = a.T;
@@ -85,25 +85,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     const float* __restrict__ cs = a.rope_cs;
     const float c2 = a.scale * kLog2e;
 
+    const int kv_end = min(T_, i0 + kQBlk);
+    const int nsteps = (kv_end + kTile - 1) / kTile;
+    // buffers over kv head bg (key rows past T read as zeros; they are causally masked)
+    const unsigned hbytes = (unsigned)T_ * (unsigned)(D * 2);
+    const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D, hbytes);
+    const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D, hbytes);
+    const unsigned lk = lds_addr(&S.k[0][0]), lv = lds_addr(&S.v[0][0]);
+    TileCopy<D> tc;
+    tc.init(w, lane);
+    auto issue = [&](int st, int buf) {
+        const unsigned row0 = (unsigned)(st * kTile) * (unsigned)(D * 2), so = (unsigned)buf * TileCopy<D>::kBytes;
+        tc.copy(rk, row0, lk + so, w);
+        tc.copy(rv, row0, lv + so, w);
+    };
+    issue(0, 0);
+    if (nsteps > 1) issue(1, 1);
+
     // this lane's query, rotated in float32 and held as two bf16 B operands (hi + lo) of
     // S^T = K~ Q~^T: the rotated query is then exact to ~2^-16 in the score product, and only the
     // rounding of the rotated keys remains (the dominant bf16 error once keys are large)
     bf16x8 qhi[NCH], qlo[NCH];
     row_operands<D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D, cs,
                     min(qrow, T_ - 1), half, qhi, qlo);
+    wait_vmcnt<0>();   // query operands and the first two tiles (see copy16_to_lds)
 
-    const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D;
-    const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D;
-    const int kv_end = min(T_, i0 + kQBlk);
-    const int nsteps = (kv_end + kTile - 1) / kTile;
-    TileLoad<D, 2, false> pf;
-    {
-        const bf16* src[2] = {kbase, vbase};
-        bf16* dst[2] = {S.k[0], S.v[0]};
-        pf.load(src, cs, 0, T_ - 1, tid);
-        pf.store(dst, cs != nullptr, tid);
-    }
-    __syncthreads();
+    // per-lane LDS offsets of the key row fragments (row 32*kt + col, chunks 2c + half)
+    int roff[2][NCH];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) roff[kt][c] = Swz<D>::at(32 * kt + col, 16 * c + 8 * half);
 
     f32x16 oacc[NDT];
 #pragma unroll
@@ -111,24 +123,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     float m_run = -INFINITY;   // reference max, log2 units
     float l_run = 0.f;         // this lane's share of the row sum (against m_run)
 
+    int buf = 0;                                      // stage of the current step
     for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
+        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
+        else wait_vmcnt<0>();
+        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
+        if (st + 2 < nsteps) issue(st + 2, buf == 0 ? 2 : buf - 1);
         const int j0 = st * kTile;
-        const bool more = st + 1 < nsteps;
-        if (more) {
-            const bf16* src[2] = {kbase + (size_t)(j0 + kTile) * D, vbase + (size_t)(j0 + kTile) * D};
-            pf.load(src, cs, j0 + kTile, T_ - 1 - j0 - kTile, tid);
-        }
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
-            // all key fragments first, then the two independent accumulation chains interleaved
+            // key fragments as one batch, then the two independent accumulation chains interleaved;
+            // the V^T fragments of the PV product are read while the softmax waits for S
             bf16x8 kf[2][NCH];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(&Ks[(32 * kt + col) * RS + 16 * c + 8 * half]);
+                for (int c = 0; c < NCH; ++c) kf[kt][c] = *reinterpret_cast<const bf16x8*>(Ks + roff[kt][c]);
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 sT[2];
             sT[0] = M::mma(kf[0][0], qhi[0], f32x16{});
             sT[1] = M::mma(kf[1][0], qhi[0], f32x16{});
@@ -141,6 +153,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                 sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
                 sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 vf[4][NDT];
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag_swz<D>(Vs, 32 * dt, kb0, kb0 + 8, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             if (j0 + kTile - 1 > wq0) {     // diagonal tile for this wave: keys after the query
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
@@ -181,24 +202,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                     else pb[pc] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             l_run += ls;
-            // O^T += V^T P^T  (V^T fragments read first)
-            bf16x8 vf[4][NDT];
-#pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag(Vs, RS, 32 * dt, kb0, kb0 + 8, lane);
-            }
+            // O^T += V^T P^T
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::mma(vf[pc][dt], pb[pc], oacc[dt]);
         }
-        if (more) {
-            bf16* dst[2] = {S.k[buf ^ 1], S.v[buf ^ 1]};
-            pf.store(dst, cs != nullptr, tid);
-        }
-        __syncthreads();
+        buf = buf == kStages - 1 ? 0 : buf + 1;
     }
 
     // epilogue: O = O^T / l, L = (m + log2 l) ln 2

@@ -8,11 +8,11 @@ namespace ne {
 
 struct FwdArgs {
     const void* q;
-    const void* k;
+    const void* k;          // bf16 kernel: keys already rotated (R k) when rope_cs is set
     const void* v;
     void* o;
     float* lse;
-    const float* rope_cs;   // [T][D/2][2] or nullptr
+    const float* rope_cs;   // [T][D/2][2] or nullptr (bf16 kernel: used for the queries only)
     int B, Hq, Hkv, T;
     float scale;
 };

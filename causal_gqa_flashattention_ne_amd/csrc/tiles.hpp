@@ -1,37 +1,30 @@
 // tiles.hpp -- LDS tile staging and operand helpers shared by the bf16 kernels (gfx950).
 //
-// Tiles of 64 rows x D (bf16, row-major, row stride D + 8 in LDS) are loaded by a 256-thread
-// workgroup, 16 bytes per thread and chunk, with row indices clamped into the sequence so the
-// loads are unconditional and nothing waits on them before the tile is stored.  The first tile
-// of a set may be rotated by RoPE on its way to LDS (queries or keys: the rotation is applied in
-// float32 and rounded to bf16 once), optionally split into a bf16 high part and a bf16 remainder.
+// Tiles of 64 rows x D bf16 go from global memory straight into LDS (buffer_load_dwordx4 ... lds:
+// no registers, no LDS store instructions) through three stages, two steps ahead of their use.
+// LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (Swz) so that row reads
+// (ds_read_b128) and transposed reads (ds_read_b64_tr_b16) stay conflict-free.  A step opens with
+// an explicit wait for this wave's copies of the current tile and one barrier without a fence.
 #pragma once
 
 #include "common.hpp"
 
 namespace ne {
 
-constexpr int kTileRows = 64;        // rows of one staged tile
-constexpr int kBlockThreads = 256;   // threads of every bf16 attention workgroup
+constexpr int kTileRows = 64;                   // rows of one staged tile
+constexpr int kBlockThreads = 256;              // threads of every bf16 attention workgroup
+constexpr int kBlockWaves = kBlockThreads / 64;
+constexpr int kStages = 3;                      // LDS stages: a tile is fetched two steps before its use
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element (i % 4) of the 8-byte
 // rows read by lanes (i / 4) + 4k, k = 0..3.
 __device__ inline bf16x4 tr_read(const bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-// A-operand fragment (32 rows m x 16 k) of the 32x32x16 MFMA taken from a row-major LDS tile
-// X[k][m] (so A[m][k] = X[k][m]): lane (m = l%32, half h) receives X[k][m] for the k rows
-// kb0 + 0..3 and kb1 + 0..3 (kb0 / kb1 chosen per half by the caller).  rs = row stride.
-__device__ inline bf16x8 tr_frag(const bf16* X, int rs, int m0, int kb0, int kb1, int lane) {
-    const int s = lane & 15;
-    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const bf16x4 lo = tr_read(X + (kb0 + (s >> 2)) * rs + m);
-    const bf16x4 hi = tr_read(X + (kb1 + (s >> 2)) * rs + m);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 packs two per instruction)
@@ -51,63 +44,97 @@ __device__ inline bf16x8 remainder8(const float* x, bf16x8 hi) {
     return cvt8(r);
 }
 
-// RoPE on 8 consecutive values (4 adjacent pairs) with their table entries (cos, sin) x 4.
-__device__ inline void rot8(bf16x8 in, const f32x4* cs, float* y) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float c = cs[p >> 1][2 * (p & 1)], s = cs[p >> 1][2 * (p & 1) + 1];
-        const float x0 = (float)in[2 * p], x1 = (float)in[2 * p + 1];
-        y[2 * p] = x0 * c - x1 * s;
-        y[2 * p + 1] = x0 * s + x1 * c;
-    }
+// Unpadded LDS tile of 64 rows x D bf16.  The 16-byte chunk c of row r is stored at chunk
+// position c ^ f(r): any 8 consecutive rows then put a given column chunk in 8 different bank
+// groups, and the 4-row x 32-byte footprint of a transposed read is spread as well.
+template <int D>
+struct Swz {
+    static constexpr int CPR = D / 8;                                  // chunks per row
+    __device__ static inline int f(int r) { return (r * CPR / 8) & (CPR - 1); }
+    // element offset of (row r, column col); a read of up to 8 elements starting at col must not
+    // cross a chunk boundary
+    __device__ static inline int at(int r, int col) { return r * D + (((col >> 3) ^ f(r)) << 3) + (col & 7); }
+};
+
+// A-operand fragment (32 rows m x 16 k) of the 32x32x16 MFMA taken from a swizzled LDS tile
+// X[k][m] (so A[m][k] = X[k][m]): lane (m = l%32, half h) receives X[k][m] for the k rows
+// kb0 + 0..3 and kb1 + 0..3 (kb0 / kb1 chosen per half by the caller).
+template <int D>
+__device__ inline bf16x8 tr_frag_swz(const bf16* X, int m0, int kb0, int kb1, int lane) {
+    const int s = lane & 15;
+    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const bf16x4 lo = tr_read(X + Swz<D>::at(kb0 + (s >> 2), m));
+    const bf16x4 hi = tr_read(X + Swz<D>::at(kb1 + (s >> 2), m));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Prefetch of NT tiles of 64 rows x D.  Tile 0 may be rotated on the store to LDS (positions of
-// its rows come with the load); with SPLIT it is stored as two tiles, bf16(R x) to dst[0] and the
-// bf16 remainder R x - bf16(R x) to dst[NT].
-template <int D, int NT, bool SPLIT>
-struct TileLoad {
-    static constexpr int NU = (kTileRows * D / 8) / kBlockThreads;
-    static constexpr int RS = D + 8;
-    static_assert((kTileRows * D / 8) % kBlockThreads == 0, "tile chunks must cover the workgroup evenly");
-    bf16x8 x[NT][NU];
-    f32x4 cs[NU][2];
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them)
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-    // Rows r0 + (0..63) of each src[t] (row-major, D per row), clamped to r0 + last; the RoPE
-    // table rows are pos0 + the same row offsets.
-    __device__ inline void load(const bf16* const* src, const float* cs_tab, int pos0, int last, int tid) {
+// Barrier between the waves of the workgroup without a memory fence (the fence of
+// __syncthreads would also wait for the copies still in flight); the empty asm keeps the
+// compiler from moving LDS accesses across it.
+__device__ inline void step_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Raw buffer descriptor (gfx9 family): base address, stride 0, size in bytes (reads at or past it
+// return zeros), 32-bit data format.  All fields are wave-uniform.
+__device__ inline i32x4 buffer_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long adr = reinterpret_cast<unsigned long long>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)adr);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(adr >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a __shared__ object (taken once per block; per-step addresses are offsets
+// from it in scalar registers).
+__device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(lds_void*)p; }
+
+// One 16-byte-per-lane copy from a buffer into LDS (buffer_load_dwordx4 ... lds): lane i reads at
+// byte voff + soff of the buffer and writes bytes 16i..16i+15 after the wave-uniform LDS byte
+// address lds.  Written as assembly so that the compiler does not track these copies: its
+// automatic wait before a transposed LDS read would otherwise also wait for the copies of the
+// tiles two steps ahead.  Every wait on them is the explicit wait_vmcnt at the top of a step; the
+// per-lane operands a kernel loads before its step loop are waited for (vmcnt(0)) before the loop
+// starts, so no other vector-memory load is in flight in it.
+__device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+
+// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles.  Each wave
+// issues D / 32 copies of 64 lanes x 16 bytes; the LDS side of one copy is a contiguous 1 KiB
+// slice, so the swizzle is applied by choosing which chunk each lane fetches.  The per-lane byte
+// offsets within a tile do not depend on the tile; rows past the end of the buffer read as zeros.
+template <int D>
+struct TileCopy {
+    static constexpr int CPR = D / 8, NU = kTileRows * CPR / (64 * kBlockWaves);
+    static_assert(NU >= 1 && (kTileRows * CPR) % (64 * kBlockWaves) == 0, "tile chunks must cover the waves evenly");
+    static constexpr unsigned kBytes = kTileRows * D * 2;   // one LDS tile
+    unsigned voff[NU];
+    __device__ inline void init(int w, int lane) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kBlockThreads;
-            const int r = min(ch / (D / 8), last), d0 = (ch % (D / 8)) * 8;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) x[t][u] = *reinterpret_cast<const bf16x8*>(src[t] + r * D + d0);
-            if (cs_tab) {
-                const f32x4* c = reinterpret_cast<const f32x4*>(cs_tab + (size_t)(pos0 + r) * D + d0);
-                cs[u][0] = c[0];
-                cs[u][1] = c[1];
-            }
+            const int idx = (u * kBlockWaves + w) * 64 + lane;
+            const int r = idx / CPR, p = idx % CPR;
+            voff[u] = (unsigned)(r * D + ((p ^ Swz<D>::f(r)) << 3)) * 2u;
         }
     }
-
-    __device__ inline void store(bf16* const* dst, bool rope, int tid) const {
+    // the tile whose first row starts at byte row0 of the buffer, into the LDS tile at byte lds
+    __device__ inline void copy(i32x4 rsrc, unsigned row0, unsigned lds, int w) const {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + u * kBlockThreads;
-            const int o = (ch / (D / 8)) * RS + (ch % (D / 8)) * 8;
-            if (rope) {
-                float y[8];
-                rot8(x[0][u], cs[u], y);
-                const bf16x8 hi = cvt8(y);
-                *reinterpret_cast<bf16x8*>(dst[0] + o) = hi;
-                if (SPLIT) *reinterpret_cast<bf16x8*>(dst[NT] + o) = remainder8(y, hi);
-            } else {
-                *reinterpret_cast<bf16x8*>(dst[0] + o) = x[0][u];
-                if (SPLIT) *reinterpret_cast<bf16x8*>(dst[NT] + o) = bf16x8{};
-            }
-#pragma unroll
-            for (int t = 1; t < NT; ++t) *reinterpret_cast<bf16x8*>(dst[t] + o) = x[t][u];
-        }
+        for (int u = 0; u < NU; ++u)
+            copy16_to_lds(rsrc, voff[u], row0, lds + (unsigned)(u * kBlockWaves + w) * 1024u);
     }
 };
 

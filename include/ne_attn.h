@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 2
+#define NE_ABI_VERSION 3
 
 enum {
     NE_OK = 0,
@@ -49,7 +49,7 @@ enum {
     NE_ERR_SHAPE = -2,       /* a size <= 0, Hq % Hkv != 0, rope table too short, ... */
     NE_ERR_UNSUPPORTED = -3, /* head_dim not in {32, 64}, unknown dtype, causal != 1 */
     NE_ERR_ALIGN = -4,       /* a pointer that is not 16-byte aligned */
-    NE_ERR_WORKSPACE = -5,   /* workspace smaller than ne_attn_bwd_workspace_bytes() */
+    NE_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure */
     NE_ERR_HIP = -6          /* the HIP runtime reported an error on launch */
 };
 
@@ -95,13 +95,21 @@ int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream
 int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream);
 
 /*
+ * Bytes of workspace ne_attn_fwd needs for these parameters (0 on a bad shape, and 0 when none is
+ * needed: float32, or no RoPE).  bf16 with RoPE: the keys rotated once per call, B*Hkv*T*D bf16.
+ */
+size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p);
+
+/*
  * Forward: o = softmax_causal(scale * (R q)(R k)^T) v and lse (natural log), per query head,
  * with kv head h / (Hq/Hkv).  q [B,Hq,T,D], k/v [B,Hkv,T,D], o [B,Hq,T,D] in dtype;
  * lse [B,Hq,T] float32.  Tiled with an online softmax: no T x T buffer exists at any point
- * (agentlenshq NanoEuler page, "커널 구현").
+ * (agentlenshq NanoEuler page, "커널 구현").  workspace: device, 16-byte aligned,
+ * >= ne_attn_fwd_workspace_bytes(p) bytes, owned by the caller (may be NULL when that is 0);
+ * contents on entry ignored, on exit unspecified.
  */
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
-                float* lse, void* stream);
+                float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of float32 workspace that ne_attn_bwd needs for these parameters (0 on a bad shape). */
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);

@@ -46,9 +46,9 @@ def params(**kw):
     return ne.make_params(**base)
 
 
-def fwd(p, q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED):
+def fwd(p, q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED, ws=ALIGNED, ws_bytes=1 << 30):
     vp = ctypes.c_void_p
-    return ne.lib().ne_attn_fwd(ctypes.byref(p), vp(q), vp(k), vp(v), vp(o), vp(lse), None)
+    return ne.lib().ne_attn_fwd(ctypes.byref(p), vp(q), vp(k), vp(v), vp(o), vp(lse), vp(ws), ws_bytes, None)
 
 
 def bwd(p, ws_bytes=1 << 30, ptrs=None):
@@ -71,6 +71,7 @@ def test_forward_rejects_bad_shapes(kw, code):
     assert fwd(params(**kw)) == code
     assert bwd(params(**kw)) == code
     assert ne.lib().ne_attn_bwd_workspace_bytes(ctypes.byref(params(**kw))) == 0
+    assert ne.lib().ne_attn_fwd_workspace_bytes(ctypes.byref(params(**kw))) == 0
 
 
 def test_causal_must_be_one():
@@ -131,3 +132,17 @@ def test_rope_entry_points_validate():
     assert L.ne_rope_apply(ctypes.byref(rp), vp(ALIGNED), vp(ALIGNED), 0, None) == -3
     rp.D, rp.pos_offset = 64, -1
     assert L.ne_rope_apply(ctypes.byref(rp), vp(ALIGNED), vp(ALIGNED), 0, None) == -2
+
+
+def test_forward_workspace():
+    p = params(B=2, Hq=4, Hkv=2, T=16, D=64)
+    assert ne.fwd_workspace_bytes(p) == 0                 # no RoPE: the keys are used as given
+    p.rope_cs, p.rope_rows = ALIGNED, 16
+    need = ne.fwd_workspace_bytes(p)
+    assert need == 2 * 2 * 16 * 64 * 2                    # bf16 rotated keys, rotated once per call
+    assert fwd(p, ws=0) == -1
+    assert fwd(p, ws=MISALIGNED) == -4
+    assert fwd(p, ws_bytes=need - 1) == -5
+    pf = params(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_F32)
+    pf.rope_cs, pf.rope_rows = ALIGNED, 16
+    assert ne.fwd_workspace_bytes(pf) == 0                # float32 rotates keys in the kernel
