@@ -110,3 +110,41 @@ def attention(q, k, v, do=None, theta=10000.0, scale=None, groups=None, nthreads
     if do is None:
         return o, L
     return o, L, dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, kv_len, theta=10000.0, scale=None):
+    """Attention of n new query tokens per sequence against a KV cache, in double.
+
+    q [B, Hq, n, D]: un-rotated queries; token i of sequence b sits at position kv_len[b] - n + i
+    and is rotated there (RoPE as in ``rope``; theta <= 0: none).  k_cache / v_cache
+    [B, Hkv, Tc, D]: keys already rotated at their own positions, and values; rows at or past
+    kv_len[b] are ignored.  Token i sees the keys 0 .. kv_len[b] - n + i (causal), with query head h
+    reading kv head h // (Hq / Hkv).  Returns (o [B, Hq, n, D], L [B, Hq, n], natural log).
+
+    This is the definition of the last n rows of ``attention`` written out directly (softmax over
+    the visible prefix; one numpy matrix product per head for the scores and one for P V); the
+    tests pin it to ``attention`` itself.
+    """
+    q, kc, vc = _d(q), _d(k_cache), _d(v_cache)
+    B, Hq, n, D = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    s = scale or 1.0 / np.sqrt(D)
+    o = np.empty_like(q)
+    L = np.empty((B, Hq, n))
+    for b in range(B):
+        lb = int(kv_len[b])
+        p0 = lb - n
+        qr = rope(q[b:b + 1], theta, pos_offset=p0)[0] if theta > 0 else q[b]
+        for h in range(Hq):
+            K = kc[b, h // G, :lb]
+            V = vc[b, h // G, :lb]
+            S = s * (qr[h] @ K.T)                       # [n, lb]
+            for i in range(n):
+                S[i, p0 + i + 1:] = -np.inf             # keys after the token's own position
+            m = S.max(axis=1, keepdims=True)
+            e = np.exp(S - m)
+            l = e.sum(axis=1, keepdims=True)
+            o[b, h] = (e / l) @ V
+            L[b, h] = (m + np.log(l))[:, 0]
+    return o, L
