@@ -27,16 +27,24 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
-           "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main")
+           "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main",
+           "ne_attn_decode_workspace_bytes", "ne_attn_decode")
 
 
 class AttnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("cache_rows", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
 
 
@@ -77,8 +85,11 @@ def lib():
         L.ne_attn_bwd.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
         L.ne_attn_bwd_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         L.ne_attn_bwd_main.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 8 + [vp, sz, vp]
+        L.ne_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
+        L.ne_attn_decode_workspace_bytes.restype = sz
+        L.ne_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 7 + [sz, vp]
         for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
-                  "ne_attn_bwd_main"):
+                  "ne_attn_bwd_main", "ne_attn_decode"):
             getattr(L, f).restype = ctypes.c_int
         if L.ne_abi_version() != ABI_VERSION:
             raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
@@ -254,3 +265,50 @@ def rope_apply(x, theta: float = 10000.0, inverse: bool = False, pos_offset: int
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+def make_decode_params(B, Hq, Hkv, n, D, cache_rows, scale=None, rope_cs=None) -> DecodeParams:
+    p = DecodeParams()
+    p.B, p.Hq, p.Hkv, p.n, p.D = B, Hq, Hkv, n, D
+    p.dtype = NE_DTYPE_BF16
+    p.cache_rows = cache_rows
+    p.scale = float(scale) if scale is not None else 0.0
+    p.rope_cs = rope_cs.data_ptr() if rope_cs is not None else None
+    p.rope_rows = rope_cs.shape[0] if rope_cs is not None else 0
+    return p
+
+
+def decode_workspace_bytes(p: DecodeParams) -> int:
+    return int(lib().ne_attn_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def attn_decode_into(p: DecodeParams, q, k_cache, v_cache, kv_len, o, lse, ws, stream=None):
+    """Decode into preallocated o / lse with the workspace tensor ws (uint8)."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_decode", lib().ne_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
+                                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), st))
+
+
+def attn_decode(q, k_cache, v_cache, kv_len, rope_theta: float = 10000.0, scale=None):
+    """Attention of n new tokens per sequence against a KV cache (bfloat16).
+
+    q [B, Hq, n, D] un-rotated; k_cache / v_cache [B, Hkv, cache_rows, D] with keys already rotated
+    at their positions; kv_len [B] int32 on the device (valid rows, the new tokens included).
+    Returns (o [B, Hq, n, D], lse [B, Hq, n] float32, natural log).
+    """
+    _need(q, "q")
+    B, Hq, n, D = q.shape
+    _need(k_cache, "k_cache", dtype=q.dtype, device=q.device)
+    _need(v_cache, "v_cache", shape=k_cache.shape, dtype=q.dtype, device=q.device)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("k_cache must be [B, Hkv, cache_rows, D]")
+    if kv_len.dtype != torch.int32 or kv_len.shape != (B,) or kv_len.device != q.device:
+        raise ValueError("kv_len must be an int32 tensor of shape [B] on the queries' device")
+    Hkv, rows = k_cache.shape[1], k_cache.shape[2]
+    cs = rope_table(rows, D, rope_theta, q.device) if rope_theta and rope_theta > 0 else None
+    p = make_decode_params(B, Hq, Hkv, n, D, rows, scale, cs)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, decode_workspace_bytes(p)), dtype=torch.uint8, device=q.device)
+    attn_decode_into(p, q, k_cache, v_cache, kv_len, o, lse, ws)
+    return o, lse

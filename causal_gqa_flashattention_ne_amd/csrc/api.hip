@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "../../include/ne_attn.h"
@@ -60,6 +61,35 @@ int dispatch(int dtype, int D, F&& f) {
                                             : f(ne::bf16{}, std::integral_constant<int, 32>{});
     else e = D == 64 ? f(float{}, std::integral_constant<int, 64>{}) : f(float{}, std::integral_constant<int, 32>{});
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+// Split-KV sizing of the decode path: enough (batch, kv head, chunk) waves to fill the chip
+// (~1024), chunks of whole 64-key tiles, at most 64 chunks (one merge lane each).
+void decode_split(const ne_decode_params* p, int* nsplit, int* chunk) {
+    const long groups = (long)p->B * p->Hkv;
+    const long want = std::min<long>(64, std::max<long>(1, (1024 + groups - 1) / groups));
+    const int tiles = (p->cache_rows + 63) / 64;
+    const int per = (int)std::max<long>(1, (tiles + want - 1) / want);      // tiles per chunk
+    *chunk = per * 64;
+    *nsplit = (tiles + per - 1) / per;
+}
+
+int check_decode(const ne_decode_params* p) {
+    if (!p) return NE_ERR_NULL;
+    if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->n <= 0 || p->D <= 0 || p->cache_rows <= 0)
+        return NE_ERR_SHAPE;
+    if (p->Hq % p->Hkv != 0 || p->n > p->cache_rows) return NE_ERR_SHAPE;
+    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
+    if (p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
+    if ((long)(p->Hq / p->Hkv) * p->n > 32) return NE_ERR_UNSUPPORTED;
+    if ((long)p->B * p->Hkv * p->cache_rows * p->D > kMaxElems) return NE_ERR_SHAPE;
+    if ((long)p->B * p->Hq * p->n * p->D > kMaxElems) return NE_ERR_SHAPE;
+    if (!isfinite(p->scale)) return NE_ERR_SHAPE;
+    if (p->rope_cs) {
+        if (p->rope_rows < p->cache_rows) return NE_ERR_SHAPE;
+        if (!aligned16(p->rope_cs)) return NE_ERR_ALIGN;
+    }
+    return NE_OK;
 }
 
 }  // namespace
@@ -139,6 +169,33 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
             return ne::launch_fwd<T, DD>(a, s);
         }
     });
+}
+
+size_t ne_attn_decode_workspace_bytes(const ne_decode_params* p) {
+    if (check_decode(p) != NE_OK) return 0;
+    int nsplit, chunk;
+    decode_split(p, &nsplit, &chunk);
+    const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+    return ((parts * p->D * sizeof(float) + 255) & ~(size_t)255) + parts * sizeof(float);
+}
+
+int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* kv_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    if (int rc = check_decode(p)) return rc;
+    if (int rc = check_ptrs({q, k_cache, v_cache, kv_len, o, lse, workspace})) return rc;
+    if (workspace_bytes < ne_attn_decode_workspace_bytes(p)) return NE_ERR_WORKSPACE;
+    int nsplit, chunk;
+    decode_split(p, &nsplit, &chunk);
+    const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+    char* ws = static_cast<char*>(workspace);
+    ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse, reinterpret_cast<float*>(ws),
+                     reinterpret_cast<float*>(ws + ((parts * p->D * sizeof(float) + 255) & ~(size_t)255)),
+                     p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows, nsplit, chunk,
+                     p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D)};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = p->D == 64 ? ne::launch_decode<64>(a, s) : ne::launch_decode<32>(a, s);
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {

@@ -40,6 +40,21 @@ struct BwdArgs {
     float scale;
 };
 
+struct DecodeArgs {
+    const void* q;          // [B, Hq, n, D] new tokens, un-rotated
+    const void* kc;         // [B, Hkv, Tc, D] keys rotated at their positions
+    const void* vc;         // [B, Hkv, Tc, D] values
+    const int* kv_len;      // [B] valid cache rows, new tokens included (clamped into [n, Tc])
+    void* o;                // [B, Hq, n, D]
+    float* lse;             // [B, Hq, n]
+    float* part_o;          // workspace: [B * Hkv][nsplit][32 columns][D] chunk outputs
+    float* part_l;          // workspace: [B * Hkv][nsplit][32 columns] chunk L (natural log)
+    const float* rope_cs;   // [rows][D/2][2] or nullptr
+    int B, Hq, Hkv, n, Tc;
+    int nsplit, chunk;      // chunks per sequence and keys per chunk (a multiple of 64)
+    float scale;
+};
+
 struct RopeArgs {
     const void* x;
     void* y;
@@ -58,6 +73,7 @@ template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t st
 template <int D> hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int D, double theta, float* cs, hipStream_t stream);
 
 }  // namespace ne

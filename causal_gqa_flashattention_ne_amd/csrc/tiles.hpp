@@ -112,20 +112,21 @@ __device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, u
                  : "memory");
 }
 
-// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles.  Each wave
-// issues D / 32 copies of 64 lanes x 16 bytes; the LDS side of one copy is a contiguous 1 KiB
-// slice, so the swizzle is applied by choosing which chunk each lane fetches.  The per-lane byte
-// offsets within a tile do not depend on the tile; rows past the end of the buffer read as zeros.
-template <int D>
+// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles by the NW waves
+// of a workgroup.  Each wave issues 64 * D / (512 * NW) copies of 64 lanes x 16 bytes; the LDS
+// side of one copy is a contiguous 1 KiB slice, so the swizzle is applied by choosing which chunk
+// each lane fetches.  The per-lane byte offsets within a tile do not depend on the tile; rows
+// past the end of the buffer read as zeros.
+template <int D, int NW = kBlockWaves>
 struct TileCopy {
-    static constexpr int CPR = D / 8, NU = kTileRows * CPR / (64 * kBlockWaves);
-    static_assert(NU >= 1 && (kTileRows * CPR) % (64 * kBlockWaves) == 0, "tile chunks must cover the waves evenly");
+    static constexpr int CPR = D / 8, NU = kTileRows * CPR / (64 * NW);
+    static_assert(NU >= 1 && (kTileRows * CPR) % (64 * NW) == 0, "tile chunks must cover the waves evenly");
     static constexpr unsigned kBytes = kTileRows * D * 2;   // one LDS tile
     unsigned voff[NU];
     __device__ inline void init(int w, int lane) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int idx = (u * kBlockWaves + w) * 64 + lane;
+            const int idx = (u * NW + w) * 64 + lane;
             const int r = idx / CPR, p = idx % CPR;
             voff[u] = (unsigned)(r * D + ((p ^ Swz<D>::f(r)) << 3)) * 2u;
         }
@@ -134,7 +135,7 @@ struct TileCopy {
     __device__ inline void copy(i32x4 rsrc, unsigned row0, unsigned lds, int w) const {
 #pragma unroll
         for (int u = 0; u < NU; ++u)
-            copy16_to_lds(rsrc, voff[u], row0, lds + (unsigned)(u * kBlockWaves + w) * 1024u);
+            copy16_to_lds(rsrc, voff[u], row0, lds + (unsigned)(u * NW + w) * 1024u);
     }
 };
 

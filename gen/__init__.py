@@ -32,7 +32,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "pick": 4}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "pick": 4, "len": 5}
 
 
 def mix64(z):
@@ -175,3 +175,17 @@ def small_case(seed, B, Hq, Hkv, T, D, dtype="f32", sigma_do=1.0, layer=0):
 
 def sha256(x: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
+
+
+def decode_case(seed, B, Hq, Hkv, n, cache_rows, D, kv_len=None, dtype="bf16"):
+    """Inputs of one decode call (tests, benchmark): the new tokens' queries q [B, Hq, n, D], raw
+    (un-rotated) keys and values of the whole cache [B, Hkv, cache_rows, D], and the valid lengths
+    kv_len [B] (given, or drawn uniformly in [n, cache_rows] per sequence).  The same N(0, 1)
+    recipe as the workloads; the caller rotates the keys into the cache."""
+    q = tensor(seed, 0, "q", (B, Hq, n, D), 1.0, dtype)
+    k = tensor(seed, 0, "k", (B, Hkv, cache_rows, D), 1.0, dtype)
+    v = tensor(seed, 0, "v", (B, Hkv, cache_rows, D), 1.0, dtype)
+    if kv_len is None:
+        draws = raw_u64(stream_key(seed, 0, TENSOR_IDS["len"]), B)
+        kv_len = [n + int(d % np.uint64(cache_rows - n + 1)) for d in draws]
+    return q, k, v, np.asarray(kv_len, dtype=np.int32)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 3
+#define NE_ABI_VERSION 4
 
 enum {
     NE_OK = 0,
@@ -147,6 +147,40 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
 int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, const void* v,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * Decode-time attention: n new tokens per sequence against a KV cache (the token-by-token
+ * generation path of the NanoEuler pages; the same attention as ne_attn_fwd at the last n
+ * positions: agentlenshq NanoEuler page, "커널 구현", RoPE as in "기술 사양").
+ *   q        [B, Hq, n, D] dtype: the new tokens' queries, un-rotated.  Token i of sequence b sits at
+ *            position kv_len[b] - n + i; it is rotated there and sees cache rows 0 .. kv_len[b] - n + i.
+ *   k_cache  [B, Hkv, cache_rows, D] dtype: keys already rotated at their own positions (rotate
+ *            each key once when appending it, e.g. ne_rope_apply with pos_offset); rows at or past
+ *            kv_len[b] are not read.  The new tokens' keys and values must be in the cache.
+ *   v_cache  [B, Hkv, cache_rows, D] dtype: values.
+ *   kv_len   [B] int32, device: valid rows per sequence, the n new tokens included.  Values outside
+ *            [n, cache_rows] are clamped into it (results are then meaningless, accesses stay in
+ *            bounds).
+ *   o [B, Hq, n, D] dtype, lse [B, Hq, n] float32 (natural log): outputs.
+ *   workspace: device, 16-byte aligned, >= ne_attn_decode_workspace_bytes(p), owned by the caller.
+ * bf16 only; D in {32, 64}; (Hq/Hkv) * n <= 32 (the query columns of one kv group share its key
+ * tiles).  Two launches on stream (split-KV chunks, then the log-sum-exp merge).
+ */
+typedef struct ne_decode_params {
+    int32_t B, Hq, Hkv;
+    int32_t n;             /* new tokens per sequence */
+    int32_t D;
+    int32_t dtype;         /* NE_DTYPE_BF16 */
+    int32_t cache_rows;    /* rows allocated per (batch, kv head) in each cache */
+    float scale;           /* <= 0: 1/sqrt(D) */
+    const float* rope_cs;  /* device RoPE table with >= cache_rows rows, or NULL (no RoPE) */
+    int32_t rope_rows;
+} ne_decode_params;
+
+size_t ne_attn_decode_workspace_bytes(const ne_decode_params* p);
+int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* kv_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 #ifdef __cplusplus
 }

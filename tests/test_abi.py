@@ -146,3 +146,47 @@ def test_forward_workspace():
     pf = params(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_F32)
     pf.rope_cs, pf.rope_rows = ALIGNED, 16
     assert ne.fwd_workspace_bytes(pf) == 0                # float32 rotates keys in the kernel
+
+
+def dparams(**kw):
+    base = dict(B=2, Hq=4, Hkv=2, n=1, D=64, cache_rows=128)
+    base.update(kw)
+    return ne.make_decode_params(**base)
+
+
+def dec(p, ws_bytes=1 << 30, ptrs=None):
+    vp = ctypes.c_void_p
+    ptrs = ptrs or [ALIGNED] * 7
+    return ne.lib().ne_attn_decode(ctypes.byref(p), *[vp(x) for x in ptrs], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2),
+    (dict(n=0), -2),
+    (dict(Hq=3), -2),
+    (dict(n=200), -2),                      # more new tokens than cache rows
+    (dict(D=48), -3),
+    (dict(n=17), -3),                       # G * n = 34 > 32 query columns
+    (dict(cache_rows=1 << 26), -2),
+])
+def test_decode_rejects_bad_shapes(kw, code):
+    p = dparams(**kw)
+    assert dec(p) == code
+    assert ne.lib().ne_attn_decode_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_decode_dtype_pointers_workspace():
+    p = dparams()
+    p.dtype = ne.NE_DTYPE_F32
+    assert dec(p) == -3                     # bf16 only
+    p = dparams()
+    need = ne.decode_workspace_bytes(p)
+    assert need > 0 and need % 4 == 0
+    assert dec(p, ws_bytes=need - 1) == -5
+    ptrs = [ALIGNED] * 7
+    ptrs[3] = 0                             # kv_len
+    assert dec(p, ptrs=ptrs) == -1
+    ptrs[3] = MISALIGNED
+    assert dec(p, ptrs=ptrs) == -4
+    p.rope_cs, p.rope_rows = ALIGNED, 127   # table shorter than the cache
+    assert dec(p) == -2
