@@ -10,6 +10,10 @@ Prints ONE JSON line.  value = whole-job algorithmic TFLOP/s with the causal pai
 14 * D * B * Hq * T(T+1)/2 per layer (forward 4*D, backward 10*D per pair).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+
+With --decode D, the step is instead one decode call (ne_attn_decode: n new tokens per sequence
+against a rotated bf16 KV cache, split over the key range and merged) on decode workload D, and
+value = algorithmic HBM GB/s of that call (cache rows read once, queries read, outputs written).
 """
 from __future__ import annotations
 
@@ -18,6 +22,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
@@ -30,6 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
+    ap.add_argument("--decode", type=int, default=0, help="decode workload id 1..2 instead of the training step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -84,6 +91,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode:
+        return bench_decode(args, dev)
     w = gen.WORKLOADS[args.workload]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4
@@ -222,14 +231,115 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.copy_calibration:
-        # a kernel of known traffic: reads 256 MiB and writes 256 MiB per launch
-        src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        out["copy_calibration"] = {"kernel": "torch.neg (elementwise)", "read_bytes": src.numel() * 2,
-                                   "write_bytes": dst.numel() * 2, "launches": 5}
+        out["copy_calibration"] = copy_calibration(dev)
+    print(json.dumps(out))
+
+
+def copy_calibration(dev):
+    """A kernel of known traffic for the HBM byte counters: reads 256 MiB and writes 256 MiB per
+    launch, 5 launches."""
+    import torch
+    src = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg (elementwise)", "read_bytes": src.numel() * 2, "write_bytes": dst.numel() * 2,
+            "launches": 5}
+
+
+def decode_bytes(w, lens):
+    """Algorithmic HBM bytes of one decode call: the valid K and V cache rows, the queries, the
+    table rows of the new tokens' positions, O and L."""
+    cache = int(np.sum(lens, dtype=np.int64)) * w.Hkv * w.D * 2 * 2
+    qo = 2 * w.B * w.Hq * w.n * w.D * 2
+    return cache + qo + w.B * w.n * w.D * 4 + w.B * w.Hq * w.n * 4
+
+
+def bench_decode(args, dev):
+    import torch
+
+    import causal_gqa_flashattention_ne_amd as ne
+    import gen
+
+    w = gen.DECODE_WORKLOADS[args.decode]
+    q, k, v, lens = gen.decode_inputs(w)
+    qd = torch.from_numpy(q).to(dev).to(torch.bfloat16).contiguous()
+    kc = ne.rope_apply(torch.from_numpy(k).to(dev).to(torch.bfloat16).contiguous(), w.theta)
+    vc = torch.from_numpy(v).to(dev).to(torch.bfloat16).contiguous()
+    kl = torch.from_numpy(lens).to(dev)
+    cs = ne.rope_table(w.cache_rows, w.D, w.theta, dev)
+    p = ne.make_decode_params(w.B, w.Hq, w.Hkv, w.n, w.D, w.cache_rows, None, cs)
+    o = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.Hq, w.n, dtype=torch.float32, device=dev)
+    ws = torch.zeros(ne.decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    st = ne.ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        ne.attn_decode_into(p, qd, kc, vc, kl, o, lse, ws, st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    # per-call durations from event pairs around every call, on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    avg_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = decode_bytes(w, lens)
+    roof = {"bound": "hbm", "achieved": nbytes / (avg_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name, "decode_split")
+    roof.update({"kernel": "decode call (split + merge)", "avg_us": avg_us, "algorithmic_bytes": nbytes})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the whole batch, one oracle call per sequence; the cache is rotated beforehand, untimed, as
+        # the GPU call also receives a rotated cache
+        kco = [oracle.rope(k[b:b + 1], w.theta) for b in range(w.B)]
+        t_s = time.perf_counter()
+        for b in range(w.B):
+            oracle.decode(q[b:b + 1], kco[b], v[b:b + 1], lens[b:b + 1], theta=w.theta)
+        dt = time.perf_counter() - t_s
+        done, nb = w.B, nbytes
+        cpu = {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "%d of %d sequences, decode in double over the oracle-rotated cache, %.2f s wall"
+                         % (done, w.B, dt)}
+
+    out = {
+        "metric": "decode attention, algorithmic HBM GB/s of one call (KV cache read once)",
+        "value": nbytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normals; ragged kv lengths uniform in [n, cache_rows])",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "n": w.n, "cache_rows": w.cache_rows,
+                   "D": w.D, "kv_len_total": int(np.sum(lens)), "rope_theta": w.theta, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": w.B * w.n / (ms * 1e-3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.copy_calibration:
+        out["copy_calibration"] = copy_calibration(dev)
     print(json.dumps(out))
 
 

@@ -283,7 +283,8 @@ def decode_workspace_bytes(p: DecodeParams) -> int:
 
 
 def attn_decode_into(p: DecodeParams, q, k_cache, v_cache, kv_len, o, lse, ws, stream=None):
-    """Decode into preallocated o / lse with the workspace tensor ws (uint8)."""
+    """Decode into preallocated o / lse with the workspace tensor ws (uint8, zero-filled before its
+    first use: every call leaves it ready for the next; one call at a time per workspace)."""
     st = stream if stream is not None else _stream(q.device)
     _check("ne_attn_decode", lib().ne_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
                                                   _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), st))
@@ -309,6 +310,6 @@ def attn_decode(q, k_cache, v_cache, kv_len, rope_theta: float = 10000.0, scale=
     p = make_decode_params(B, Hq, Hkv, n, D, rows, scale, cs)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
-    ws = torch.empty(max(1, decode_workspace_bytes(p)), dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(max(1, decode_workspace_bytes(p)), dtype=torch.uint8, device=q.device)
     attn_decode_into(p, q, k_cache, v_cache, kv_len, o, lse, ws)
     return o, lse

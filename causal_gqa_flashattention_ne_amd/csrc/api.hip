@@ -74,6 +74,29 @@ void decode_split(const ne_decode_params* p, int* nsplit, int* chunk) {
     *nsplit = (tiles + per - 1) / per;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// at most 16 query columns per kv group: the balanced 16-column path
+bool decode_narrow(const ne_decode_params* p) { return (long)(p->Hq / p->Hkv) * p->n <= 16; }
+
+// Workspace of the 16-column path: arrival counters (zero between calls), then piece L and O for
+// up to wcap waves plus one slot per segment.
+struct Decode16Layout {
+    long max_tiles;   // tiles when every cache is full
+    int wcap;         // cap on the grid's waves
+    size_t ctr, part_l, part_o, total;
+    explicit Decode16Layout(const ne_decode_params* p) {
+        const long nseg = (long)p->B * p->Hkv;
+        max_tiles = nseg * ((p->cache_rows + ne::kDecodeTileRows - 1) / ne::kDecodeTileRows);
+        wcap = (int)std::min<long>(ne::kDecodeMaxWaves, max_tiles);
+        const size_t slots = (size_t)wcap + nseg;
+        ctr = 0;
+        part_l = align256(nseg * sizeof(int));
+        part_o = part_l + align256(slots * 16 * sizeof(float));
+        total = part_o + slots * 16 * p->D * sizeof(float);
+    }
+};
+
 int check_decode(const ne_decode_params* p) {
     if (!p) return NE_ERR_NULL;
     if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->n <= 0 || p->D <= 0 || p->cache_rows <= 0)
@@ -173,10 +196,11 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
 
 size_t ne_attn_decode_workspace_bytes(const ne_decode_params* p) {
     if (check_decode(p) != NE_OK) return 0;
+    if (decode_narrow(p)) return Decode16Layout(p).total;
     int nsplit, chunk;
     decode_split(p, &nsplit, &chunk);
     const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
-    return ((parts * p->D * sizeof(float) + 255) & ~(size_t)255) + parts * sizeof(float);
+    return align256(parts * p->D * sizeof(float)) + parts * sizeof(float);
 }
 
 int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
@@ -185,16 +209,30 @@ int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache
     if (int rc = check_decode(p)) return rc;
     if (int rc = check_ptrs({q, k_cache, v_cache, kv_len, o, lse, workspace})) return rc;
     if (workspace_bytes < ne_attn_decode_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    int nsplit, chunk;
-    decode_split(p, &nsplit, &chunk);
-    const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+    const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
     char* ws = static_cast<char*>(workspace);
-    ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse, reinterpret_cast<float*>(ws),
-                     reinterpret_cast<float*>(ws + ((parts * p->D * sizeof(float) + 255) & ~(size_t)255)),
-                     p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows, nsplit, chunk,
-                     p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D)};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = p->D == 64 ? ne::launch_decode<64>(a, s) : ne::launch_decode<32>(a, s);
+    hipError_t e;
+    if (decode_narrow(p)) {
+        const Decode16Layout L(p);
+        const int slots = p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
+        if (slots <= 0) return NE_ERR_HIP;
+        // at least two tiles per wave when every cache is full; never more waves than fit at once
+        const long waves = std::min<long>({(long)L.wcap, (L.max_tiles + 1) / 2, (long)slots});
+        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse,
+                         reinterpret_cast<float*>(ws + L.part_o), reinterpret_cast<float*>(ws + L.part_l),
+                         reinterpret_cast<int*>(ws + L.ctr), p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows,
+                         (int)std::max<long>(1, waves), 0, scale};
+        e = p->D == 64 ? ne::launch_decode16<64>(a, s) : ne::launch_decode16<32>(a, s);
+    } else {
+        int nsplit, chunk;
+        decode_split(p, &nsplit, &chunk);
+        const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse, reinterpret_cast<float*>(ws),
+                         reinterpret_cast<float*>(ws + align256(parts * p->D * sizeof(float))), nullptr,
+                         p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows, nsplit, chunk, scale};
+        e = p->D == 64 ? ne::launch_decode<64>(a, s) : ne::launch_decode<32>(a, s);
+    }
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 

@@ -15,6 +15,9 @@
 // decode_merge then combines the chunks by log-sum-exp:
 //     L = log sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s.
 // The work is a stream over the cache: HBM-bound, the matrix cores idle most of the time.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
@@ -234,6 +237,372 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     if (lane == 0) a.lse[row] = mx + __logf(sum);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Balanced path for at most 16 query columns per kv group (G * n <= 16: the usual decode, where a
+// kv head serves a few query heads and one or a few new tokens).
+//
+// The products use the 16 x 16 x 32 bf16 MFMA (result (i, j) in lane j + 16 (i / 4), register
+// i % 4), so a 16-column group costs half the matrix work and half the softmax values of the
+// 32-column layout.  Lane (c = lane % 16, g = lane / 16) owns query column c:
+//   S^T = K~ Q~^T   A = K~ rows (key 16 kb + lane % 16, d = 32 ks + 8 g + 0..7), B = Q~ operands;
+//                   lane (c, g) receives the scores of keys 16 kb + 4 g + 0..3;
+//   O^T += V^T P^T  k slot 8 g + e of step k2 is key 32 k2 + 4 g + e (e < 4) or
+//                   32 k2 + 16 + 4 g + e - 4 (e >= 4): exactly the scores lane (c, g) holds, so P^T
+//                   is its own B operand; V^T comes from transposed LDS reads in the same order.
+//
+// Work split: the (batch, kv head) segments of valid tiles are laid end to end (sequence-major,
+// kv head inside) and the W waves of the grid take equal shares [w T / W, (w + 1) T / W) of that
+// line, T the total, whatever the mix of cache lengths.  A wave walks the segment pieces of its
+// share.  A piece that is a whole segment writes O and L directly; otherwise it writes its
+// normalised O and its L to partial slot w + segment (slots are unique along the line), and the
+// last piece of the segment to arrive, counted on a per-segment arrival counter, merges all of
+// them by log-sum-exp and resets the counter to zero for the next call.
+template <int D, int TR, int NS>
+struct alignas(16) Dec16Lds {
+    alignas(16) bf16 k[NS][TR * D];    // K~ tiles [key][d] (swizzled)
+    alignas(16) bf16 v[NS][TR * D];    // V tiles
+};
+
+__device__ inline float pair16_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair16_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// max / sum over the four lanes (c, g = 0..3) of a column
+__device__ inline float col_max(float x) { return partner_max(pair16_max(x)); }
+__device__ inline float col_sum(float x) { return partner_sum(pair16_sum(x)); }
+
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ inline int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// wait until at most `ahead` (0 .. MAXA) tiles of KC copies each are still in flight
+template <int KC, int MAXA>
+__device__ inline void wait_tiles(int ahead) {
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * KC>();
+            return;
+        }
+        wait_tiles<KC, MAXA - 1>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// Q~ operands of one query row for the 16 x 16 x 32 layout: lane group g supplies
+// d = 32 ks + 8 g + 0..7, rotated to R_pos q in float32 and split into bf16 hi + lo.
+template <int D>
+__device__ inline void q_operands16(const bf16* rowp, const float* cs, int pos, int g, bf16x8* hi, bf16x8* lo) {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        float x[8];
+        const int d0 = 32 * ks + 8 * g;
+        load16<bf16>(rowp + d0, x);
+        if (cs) rope_rotate(x, 8, cs, D, pos, d0, false);
+        hi[ks] = cvt8(x);
+        lo[ks] = remainder8(x, hi[ks]);
+    }
+}
+
+// a value every lane holds alike, moved to scalar registers
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline long long uniform(long long x) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)x);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ inline int valid_rows(const DecodeArgs& a, int b) { return min(max(a.kv_len[b], a.n), a.Tc); }
+
+// Wave w's share of the line is [floor(w T / W), floor((w + 1) T / W)); shares are empty only
+// when T < W, and then every non-empty share is a single tile.
+// the wave whose share holds line position x: the largest w with floor(w T / W) <= x
+__device__ inline int wave_of(long long x, long long total, int W) {
+    return (int)(((x + 1) * W - 1) / total);
+}
+
+template <int D, int TR, int NS>
+__global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
+    constexpr int KB = TR / 16, KS = D / 32, DB = D / 16, K2 = TR / 32;
+    using TC = TileCopy<D, 1, TR>;
+    constexpr int kCopies = 2 * TC::NU;          // copies per tile (K~ and V)
+    static_assert(NS >= 2 && (NS - 1) * kCopies < 64, "copies in flight must fit vmcnt");
+    __shared__ Dec16Lds<D, TR, NS> S;
+
+    const int lane = threadIdx.x, c = lane & 15, g4 = lane >> 4;
+    const int W = a.nsplit, w = (int)blockIdx.x;
+    const int G = a.Hq / a.Hkv, ncol = G * a.n;
+
+    // ---- this wave's share of the tile line ----
+    // tiles of sequence b0 + lane and their inclusive prefix over the chunk of 64 sequences
+    auto chunk_tiles = [&](int b0, int& tl, int& incl) {
+        tl = b0 + lane < a.B ? (valid_rows(a, b0 + lane) + TR - 1) / TR : 0;
+        incl = wave_incl_scan(tl, lane);
+    };
+    int tl, incl;
+    chunk_tiles(0, tl, incl);
+    long long total = __builtin_amdgcn_readlane(incl, 63);
+    for (int b0 = 64; b0 < a.B; b0 += 64) {
+        int t2, i2;
+        chunk_tiles(b0, t2, i2);
+        total += __builtin_amdgcn_readlane(i2, 63);
+    }
+    total = uniform(total * a.Hkv);
+    const long long lo = (long long)w * total / W, hi = (long long)(w + 1) * total / W;
+    if (lo >= hi) return;
+    int b = 0;
+    long long pb = 0;                             // line position of sequence b's first segment
+    for (int b0 = 0;; b0 += 64) {
+        if (b0 > 0) chunk_tiles(b0, tl, incl);
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(b0 + lane < a.B && pb + (long long)a.Hkv * incl > lo);
+        if (m) {
+            const int f = __builtin_ctzll(m);
+            b = b0 + f;
+            pb += (long long)a.Hkv * (__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(tl, f));
+            break;
+        }
+        pb += (long long)a.Hkv * __builtin_amdgcn_readlane(incl, 63);
+    }
+    b = uniform(b);
+    pb = uniform(pb);
+    int lb = valid_rows(a, b), nt_b = (lb + TR - 1) / TR;
+    int g = (int)((lo - pb) / nt_b), t0 = (int)((lo - pb) % nt_b);
+
+    const unsigned lk = lds_addr(&S.k[0][0]), lv = lds_addr(&S.v[0][0]);
+    TC tc;
+    tc.init(0, lane);
+    int roff[KB][KS], voff[K2][2][DB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) roff[kb][ks] = Swz<D>::at(16 * kb + c, 32 * ks + 8 * g4);
+#pragma unroll
+    for (int k2 = 0; k2 < K2; ++k2)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                voff[k2][h][db] = Swz<D>::at(32 * k2 + 16 * h + 4 * g4 + (c >> 2), 16 * db + 4 * (c & 3));
+    const float c2 = a.scale * kLog2e;
+    const float* __restrict__ cs = a.rope_cs;
+    // this lane's query column: head g G + hh, token ti (columns past G n repeat column 0 and are
+    // never stored)
+    const int cc = c < ncol ? c : 0;
+    const int hh = cc / a.n, ti = cc % a.n;
+
+    for (long long x = lo;;) {
+        // ---- piece: tiles [t0, t1) of segment (b, g) ----
+        const int t1 = (int)min((long long)nt_b, t0 + (hi - x));
+        const int seg = b * a.Hkv + g;
+        const int k0 = t0 * TR, k1 = min(t1 * TR, lb), nt = t1 - t0;
+        const unsigned hbytes = (unsigned)lb * (unsigned)(D * 2);
+        const size_t hoff = (size_t)seg * a.Tc * D;
+        const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.kc) + hoff, hbytes);
+        const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.vc) + hoff, hbytes);
+        auto issue = [&](int i) {
+            const unsigned row0 = (unsigned)(k0 + i * TR) * (unsigned)(D * 2);
+            const unsigned so = (unsigned)(i % NS) * TC::kBytes;
+            tc.copy(rk, row0, lk + so, 0);
+            tc.copy(rv, row0, lv + so, 0);
+        };
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < nt) issue(i);
+        const int pos = lb - a.n + ti;
+        bf16x8 qhi[KS], qlo[KS];
+        q_operands16<D>(reinterpret_cast<const bf16*>(a.q) + (((size_t)b * a.Hq + g * G + hh) * a.n + ti) * D, cs, pos,
+                        g4, qhi, qlo);
+        wait_vmcnt<0>();   // query operands and the first tiles (see copy16_to_lds)
+
+        f32x4 oacc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int i = 0; i < nt; ++i) {
+            wait_tiles<kCopies, NS - 2>(nt - 1 - i);
+            if (i + NS - 1 < nt) issue(i + NS - 1);   // its stage was last read in step i - 1
+            const int buf = i % NS;
+            const int j0 = k0 + i * TR;
+            const bf16* Ks = S.k[buf];
+            const bf16* Vs = S.v[buf];
+            bf16x8 kf[KB][KS];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *reinterpret_cast<const bf16x8*>(Ks + roff[kb][ks]);
+            f32x4 sc[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sc[kb] = mma16(kf[kb][0], qhi[0], f32x4{});
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sc[kb] = mma16(kf[kb][0], qlo[0], sc[kb]);
+#pragma unroll
+            for (int ks = 1; ks < KS; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sc[kb] = mma16(kf[kb][ks], qhi[ks], sc[kb]);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sc[kb] = mma16(kf[kb][ks], qlo[ks], sc[kb]);
+            }
+            bf16x8 vf[K2][DB];
+#pragma unroll
+            for (int k2 = 0; k2 < K2; ++k2)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    vf[k2][db] = __builtin_shufflevector(tr_read(Vs + voff[k2][0][db]), tr_read(Vs + voff[k2][1][db]),
+                                                         0, 1, 2, 3, 4, 5, 6, 7);
+            // keys past the piece or after this column's token are invisible (S = -inf for the
+            // max, P = 0)
+            const bool edge = j0 + TR > k1 || j0 + TR - 1 > lb - a.n;
+            unsigned vis = ~0u;                         // bit 4 kb + e: key 16 kb + 4 g + e visible
+            if (edge) {
+                vis = 0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0 + 16 * kb + 4 * g4 + e;
+                        if (j < k1 && j <= pos) vis |= 1u << (4 * kb + e);
+                        else sc[kb][e] = -INFINITY;
+                    }
+            }
+            float mx = sc[0][0];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[kb][e]);
+            mx = col_max(mx) * c2;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescale) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+                m_run = m_new;
+            }
+            float ls = 0.f;
+#pragma unroll
+            for (int k2 = 0; k2 < K2; ++k2) {
+                float p[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int kb = 2 * k2 + h;
+                        p[4 * h + e] = (vis >> (4 * kb + e)) & 1
+                                           ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e], c2, -m_run)) : 0.f;
+                        ls += p[4 * h + e];
+                    }
+                const bf16x8 pb = cvt8(p);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] = mma16(vf[k2][db], pb, oacc[db]);
+            }
+            l_run += ls;
+        }
+
+        // ---- the piece's result ----
+        const float l_tot = col_sum(l_run);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float L = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        const long long ps = pb + (long long)g * nt_b;                // the segment on the line
+        const int wf = wave_of(ps, total, W), wl = wave_of(ps + nt_b - 1, total, W);
+        const int npieces = total >= W ? wl - wf + 1 : nt_b;         // waves holding part of it
+        const size_t orow = ((size_t)b * a.Hq + g * G + hh) * a.n + ti;
+        if (npieces == 1) {
+            if (c < ncol) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const float y[4] = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + orow * D + 16 * db + 4 * g4) = cvt4(y);
+                }
+                if (g4 == 0) a.lse[orow] = L;
+            }
+        } else {
+            // Partial results cross waves (and XCDs, whose L2 caches are not coherent with each
+            // other) through device-scope atomic stores and loads, which are coherent at that
+            // scope without the L2 write-back and invalidation of a device-scope fence: the
+            // stores complete (vmcnt 0) before the arrival count is raised, and the last arrival
+            // issues its loads only once the count has come back.
+            const size_t slot = (size_t)w + seg;
+            float* __restrict__ po = a.part_o + (slot * 16 + c) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __hip_atomic_store(po + 16 * db + 4 * g4 + e, oacc[db][e] * inv, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (g4 == 0) __hip_atomic_store(a.part_l + slot * 16 + c, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_vmcnt<0>();
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.ctr + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = uniform(old);                        // lane 0's value
+            if (old == npieces - 1) {                  // the last piece of the segment: merge
+                auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+                // the waves holding the pieces, in line order: wf .. wl when no share is empty,
+                // else one wave per tile
+                const bool dense = total >= W;
+                const int np = npieces;
+                auto piece_wave = [&](int k) { return dense ? wf + k : wave_of(ps + k, total, W); };
+                float mx = -INFINITY;
+                for (int k = 0; k < np; ++k) mx = fmaxf(mx, ld(a.part_l + ((size_t)piece_wave(k) + seg) * 16 + c));
+                float sum = 0.f;
+                f32x4 acc[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+                for (int k = 0; k < np; ++k) {
+                    const size_t sl = (size_t)piece_wave(k) + seg;
+                    const float lv_ = ld(a.part_l + sl * 16 + c);
+                    const float wt = lv_ == -INFINITY ? 0.f : __expf(lv_ - mx);   // mx is finite: key 0 is seen
+                    sum += wt;
+                    const float* pv = a.part_o + (sl * 16 + c) * D;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[db][e] += wt * ld(pv + 16 * db + 4 * g4 + e);
+                }
+                if (c < ncol) {
+                    const float is = 1.f / sum;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const float y[4] = {acc[db][0] * is, acc[db][1] * is, acc[db][2] * is, acc[db][3] * is};
+                        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + orow * D + 16 * db + 4 * g4) = cvt4(y);
+                    }
+                    if (g4 == 0) a.lse[orow] = mx + __logf(sum);
+                }
+                if (lane == 0) __hip_atomic_store(a.ctr + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+
+        x += nt;
+        if (x >= hi) break;
+        t0 = 0;
+        if (++g == a.Hkv) {
+            g = 0;
+            pb += (long long)a.Hkv * nt_b;
+            ++b;
+            lb = valid_rows(a, b);
+            nt_b = (lb + TR - 1) / TR;
+        }
+    }
+}
+
 }  // namespace
 
 template <int D>
@@ -247,6 +616,38 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D>
+int decode16_slots() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&decode16_kernel<D, kDecodeTileRows, kDecodeStages>), 64, 0) !=
+        hipSuccess)
+        return 0;
+    const int v = std::max(1, cus * per_cu);
+    if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int D>
+hipError_t launch_decode16(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages>), dim3((unsigned)a.nsplit), dim3(64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template int decode16_slots<64>();
+template int decode16_slots<32>();
+template hipError_t launch_decode16<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode16<32>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode<32>(const DecodeArgs&, hipStream_t);
 

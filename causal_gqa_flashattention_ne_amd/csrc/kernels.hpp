@@ -47,13 +47,23 @@ struct DecodeArgs {
     const int* kv_len;      // [B] valid cache rows, new tokens included (clamped into [n, Tc])
     void* o;                // [B, Hq, n, D]
     float* lse;             // [B, Hq, n]
-    float* part_o;          // workspace: [B * Hkv][nsplit][32 columns][D] chunk outputs
-    float* part_l;          // workspace: [B * Hkv][nsplit][32 columns] chunk L (natural log)
+    // workspace.  32-column path: part_o [B * Hkv][nsplit][32][D] chunk outputs, part_l
+    // [B * Hkv][nsplit][32] chunk L (natural log).  16-column path: part_o [W + B * Hkv][16][D] and
+    // part_l [W + B * Hkv][16] piece results, ctr [B * Hkv] arrival counters (zero between calls).
+    float* part_o;
+    float* part_l;
+    int* ctr;
     const float* rope_cs;   // [rows][D/2][2] or nullptr
     int B, Hq, Hkv, n, Tc;
-    int nsplit, chunk;      // chunks per sequence and keys per chunk (a multiple of 64)
+    int nsplit, chunk;      // 32-column path: chunks per sequence and keys per chunk (a multiple of
+                            // 64); 16-column path: nsplit = W, the waves of the grid
     float scale;
 };
+
+// 16-column decode path: keys per staged tile, LDS stages, and the cap on the grid's waves
+constexpr int kDecodeTileRows = 64;
+constexpr int kDecodeStages = 3;
+constexpr int kDecodeMaxWaves = 4096;
 
 struct RopeArgs {
     const void* x;
@@ -74,6 +84,10 @@ template <int D> hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t s
 template <typename T, int D> hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// waves of the 16-column decode grid that fit on the current device at once (CUs x resident
+// waves per CU), or 0 when the query fails
+template <int D> int decode16_slots();
+template <int D> hipError_t launch_decode16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int D, double theta, float* cs, hipStream_t stream);
 
 }  // namespace ne

@@ -68,11 +68,13 @@ __device__ inline bf16x8 tr_frag_swz(const bf16* X, int m0, int kb0, int kb1, in
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them)
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them).  The empty asm
+// keeps the compiler from moving the LDS reads of the tile waited for above the wait.
 template <int N>
 __device__ inline void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
 }
 
 // Barrier between the waves of the workgroup without a memory fence (the fence of
@@ -112,16 +114,16 @@ __device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, u
                  : "memory");
 }
 
-// Copies of 64-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles by the NW waves
-// of a workgroup.  Each wave issues 64 * D / (512 * NW) copies of 64 lanes x 16 bytes; the LDS
+// Copies of ROWS-row x D bf16 tiles of a row-major matrix into swizzled LDS tiles by the NW waves
+// of a workgroup.  Each wave issues ROWS * D / (512 * NW) copies of 64 lanes x 16 bytes; the LDS
 // side of one copy is a contiguous 1 KiB slice, so the swizzle is applied by choosing which chunk
 // each lane fetches.  The per-lane byte offsets within a tile do not depend on the tile; rows
 // past the end of the buffer read as zeros.
-template <int D, int NW = kBlockWaves>
+template <int D, int NW = kBlockWaves, int ROWS = kTileRows>
 struct TileCopy {
-    static constexpr int CPR = D / 8, NU = kTileRows * CPR / (64 * NW);
-    static_assert(NU >= 1 && (kTileRows * CPR) % (64 * NW) == 0, "tile chunks must cover the waves evenly");
-    static constexpr unsigned kBytes = kTileRows * D * 2;   // one LDS tile
+    static constexpr int CPR = D / 8, NU = ROWS * CPR / (64 * NW);
+    static_assert(NU >= 1 && (ROWS * CPR) % (64 * NW) == 0, "tile chunks must cover the waves evenly");
+    static constexpr unsigned kBytes = ROWS * D * 2;        // one LDS tile
     unsigned voff[NU];
     __device__ inline void init(int w, int lane) {
 #pragma unroll

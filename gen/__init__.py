@@ -189,3 +189,33 @@ def decode_case(seed, B, Hq, Hkv, n, cache_rows, D, kv_len=None, dtype="bf16"):
         draws = raw_u64(stream_key(seed, 0, TENSOR_IDS["len"]), B)
         kv_len = [n + int(d % np.uint64(cache_rows - n + 1)) for d in draws]
     return q, k, v, np.asarray(kv_len, dtype=np.int32)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode call: n new tokens per sequence against a cache of cache_rows rows per kv head,
+    valid lengths kv_len drawn uniformly in [n, cache_rows] (a ragged serving batch) unless full."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    n: int
+    cache_rows: int
+    D: int
+    full: bool = False
+    theta: float = 10000.0
+    seed: int = 0
+
+
+# Decode shapes: the 116M model's attention heads (12 query heads over 4 kv heads, d = 64) at its
+# own context of 512 positions, and a serving batch over longer caches.
+DECODE_WORKLOADS = {
+    1: DecodeWorkload("gpt116m-decode-b16-ctx512", 16, 12, 4, 1, 512, 64, full=True, seed=11),
+    2: DecodeWorkload("gpt116m-heads-decode-b64-cache4096", 64, 12, 4, 1, 4096, 64, seed=12),
+}
+
+
+def decode_inputs(w: DecodeWorkload):
+    """(q, k, v, kv_len) of decode workload w (k un-rotated; the caller rotates it into the cache)."""
+    return decode_case(w.seed, w.B, w.Hq, w.Hkv, w.n, w.cache_rows, w.D,
+                       [w.cache_rows] * w.B if w.full else None)

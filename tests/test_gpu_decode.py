@@ -55,6 +55,11 @@ CASES = [
     (6, 2, 2, 2, 32, 96, 64, [32, 96]),        # G = 1, n = 32
     (7, 2, 4, 2, 3, 130, 32, [64, 65]),        # D = 32; lengths at a tile boundary
     (8, 4, 4, 2, 2, 4096, 64, None),           # long ragged caches
+    (10, 100, 2, 1, 1, 130, 64, None),         # more sequences than lanes in the length scan
+    (11, 1, 3, 1, 1, 8192, 64, [8192]),        # one sequence shared by many waves, merged
+    (12, 1, 3, 1, 5, 130, 64, [65]),           # a last piece no column of the first tokens sees
+    (13, 3, 16, 1, 1, 700, 64, [700, 1, 333]), # G = 16: the widest 16-column group
+    (14, 2, 8, 2, 2, 1000, 64, [100, 200]),    # fewer valid tiles than waves: one-tile shares
 ]
 
 
@@ -95,3 +100,25 @@ def test_decode_deterministic():
     o1, l1 = ne.attn_decode(*args)
     o2, l2 = ne.attn_decode(*args)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_workspace_reuse():
+    """One workspace across calls of different lengths: the per-segment arrival counters of the
+    16-column path are left at zero by every call."""
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, n, rows, D = 3, 6, 2, 1, 3000, 64
+    p = ne.make_decode_params(B, Hq, Hkv, n, D, rows, None, ne.rope_table(rows, D, 10000.0, dev))
+    ws = torch.zeros(ne.decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    for i, lens in enumerate(([3000, 2000, 1000], [17, 2999, 640], [3000, 3000, 3000])):
+        q, k, v, lv = gen.decode_case(50 + i, B, Hq, Hkv, n, rows, D, lens)
+        kc = gen.round_bf16(oracle.rope(k, 10000.0).astype(np.float32))
+        o_ref, L_ref = oracle.decode(q, kc, v, lv, theta=10000.0)
+        qd = bf16(q, dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(B, Hq, n, dtype=torch.float32, device=dev)
+        ne.attn_decode_into(p, qd, bf16(kc, dev), bf16(v, dev), torch.from_numpy(lv).to(dev), o, lse, ws)
+        torch.cuda.synchronize()
+        e_o = np.abs(o.float().cpu().numpy() - o_ref).max() / np.abs(o_ref).max()
+        e_l = np.abs(lse.cpu().numpy() - L_ref).max() / np.abs(L_ref).max()
+        log("  reuse call %d lens %s: e(O) %.2e e(L) %.2e" % (i, lens, e_o, e_l))
+        assert e_o <= TOL and e_l <= TOL
