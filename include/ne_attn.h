@@ -163,8 +163,14 @@ int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, cons
  *            bounds).
  *   o [B, Hq, n, D] dtype, lse [B, Hq, n] float32 (natural log): outputs.
  *   workspace: device, 16-byte aligned, >= ne_attn_decode_workspace_bytes(p), owned by the caller.
+ *            It must be zero-filled before its first use; every call leaves it ready for the
+ *            next one (arrival counters back at zero).  Calls that share a workspace must not
+ *            overlap in time.
  * bf16 only; D in {32, 64}; (Hq/Hkv) * n <= 32 (the query columns of one kv group share its key
- * tiles).  Two launches on stream (split-KV chunks, then the log-sum-exp merge).
+ * tiles).  With (Hq/Hkv) * n <= 16: one launch on stream; the valid tiles of all (sequence, kv
+ * head) pairs are split evenly over the waves that fit on the device, and the pieces of a pair
+ * are merged by log-sum-exp inside the launch.  Otherwise two launches (fixed key chunks, then
+ * the merge).  Returns NE_ERR_HIP if the device cannot be queried or a launch fails.
  */
 typedef struct ne_decode_params {
     int32_t B, Hq, Hkv;
