@@ -97,6 +97,23 @@ struct Decode16Layout {
     }
 };
 
+// Waves of the 16-column grid (never more than fit at once): the fewest that minimise the
+// estimated time with every cache full, a wave's tiles (one step each) plus the merge of a
+// segment's pieces (one round of loads, costed like a step, per kDecodeMergeBatch pieces).
+// Scans the tiles per wave k upward from the smallest feasible one; the cost is at least k.
+long decode16_waves(const ne_decode_params* p, const Decode16Layout& L, int slots) {
+    const long seg_tiles = (p->cache_rows + ne::kDecodeTileRows - 1) / ne::kDecodeTileRows;
+    const long wmax = std::max<long>(1, std::min<long>(L.wcap, slots));
+    long best = 1, best_cost = -1;
+    for (long k = (L.max_tiles + wmax - 1) / wmax; best_cost < 0 || k <= best_cost; ++k) {
+        const long w = (L.max_tiles + k - 1) / k;                       // fewest waves with <= k tiles
+        const long pieces = k >= seg_tiles ? 1 : (seg_tiles + k - 1) / k + 1;
+        const long cost = k + (pieces > 1 ? (pieces + ne::kDecodeMergeBatch - 1) / ne::kDecodeMergeBatch : 0);
+        if (best_cost < 0 || cost <= best_cost) best = w, best_cost = cost;   // ties: fewer waves
+    }
+    return best;
+}
+
 int check_decode(const ne_decode_params* p) {
     if (!p) return NE_ERR_NULL;
     if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->n <= 0 || p->D <= 0 || p->cache_rows <= 0)
@@ -217,8 +234,7 @@ int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache
         const Decode16Layout L(p);
         const int slots = p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
         if (slots <= 0) return NE_ERR_HIP;
-        // at least two tiles per wave when every cache is full; never more waves than fit at once
-        const long waves = std::min<long>({(long)L.wcap, (L.max_tiles + 1) / 2, (long)slots});
+        const long waves = decode16_waves(p, L, slots);
         ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse,
                          reinterpret_cast<float*>(ws + L.part_o), reinterpret_cast<float*>(ws + L.part_l),
                          reinterpret_cast<int*>(ws + L.ctr), p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows,

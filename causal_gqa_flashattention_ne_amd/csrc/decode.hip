@@ -308,15 +308,37 @@ __device__ inline void wait_tiles(int ahead) {
 }
 
 // Q~ operands of one query row for the 16 x 16 x 32 layout: lane group g supplies
-// d = 32 ks + 8 g + 0..7, rotated to R_pos q in float32 and split into bf16 hi + lo.
-template <int D>
+// d = 32 ks + 8 g + 0..7, rotated to R_pos q in float32 (ROPE) and split into bf16 hi + lo.  All
+// loads are issued before any is used.
+template <int D, bool ROPE>
 __device__ inline void q_operands16(const bf16* rowp, const float* cs, int pos, int g, bf16x8* hi, bf16x8* lo) {
+    constexpr int KS = D / 32;
+    bf16x8 raw[KS];
+    f32x4 cv[KS][2];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = *reinterpret_cast<const bf16x8*>(rowp + 32 * ks + 8 * g);
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                cv[ks][h] = *reinterpret_cast<const f32x4*>(cs + (size_t)pos * D + 32 * ks + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
         float x[8];
-        const int d0 = 32 * ks + 8 * g;
-        load16<bf16>(rowp + d0, x);
-        if (cs) rope_rotate(x, 8, cs, D, pos, d0, false);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)raw[ks][e];
+        if constexpr (ROPE) {
+            // pairs (x[2p], x[2p+1]) with table entry (cos, sin) = cv[ks][p / 2][2 (p % 2) + 0..1]
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const float co = cv[ks][pp >> 1][2 * (pp & 1)], si = cv[ks][pp >> 1][2 * (pp & 1) + 1];
+                const float x0 = x[2 * pp], x1 = x[2 * pp + 1];
+                x[2 * pp] = x0 * co - x1 * si;
+                x[2 * pp + 1] = x0 * si + x1 * co;
+            }
+        }
         hi[ks] = cvt8(x);
         lo[ks] = remainder8(x, hi[ks]);
     }
@@ -331,6 +353,10 @@ __device__ inline long long uniform(long long x) {
 }
 
 __device__ inline int valid_rows(const DecodeArgs& a, int b) { return min(max(a.kv_len[b], a.n), a.Tc); }
+// through a read-only, unaliased kernel argument: a scalar load for a wave-uniform b
+__device__ inline int valid_rows(const DecodeArgs& a, const int* __restrict__ kv_len, int b) {
+    return min(max(kv_len[b], a.n), a.Tc);
+}
 
 // Wave w's share of the line is [floor(w T / W), floor((w + 1) T / W)); shares are empty only
 // when T < W, and then every non-empty share is a single tile.
@@ -339,8 +365,48 @@ __device__ inline int wave_of(long long x, long long total, int W) {
     return (int)(((x + 1) * W - 1) / total);
 }
 
-template <int D, int TR, int NS>
-__global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
+// Piece results cross waves, and XCDs whose L2 caches are not coherent with each other, through
+// device-scope (sc1) buffer stores and loads, coherent at that scope without the L2 write-back
+// and invalidation of a device-scope fence.  Slot layout: O as [DB][64 lanes][4] floats (each
+// instruction moves 1 KiB contiguously), L as [16 columns].
+constexpr int kDeviceScope = 16;                 // buffer cache policy: sc1
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // the builtins' raw 128-bit data
+template <int D>
+__device__ inline __amdgpu_buffer_rsrc_t part_o_rsrc(const DecodeArgs& a, size_t slot) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part_o + slot * 16 * D, 0, 16 * D * 4, 0x00020000);
+}
+__device__ inline __amdgpu_buffer_rsrc_t part_l_rsrc(const DecodeArgs& a, size_t slot) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part_l + slot * 16, 0, 16 * 4, 0x00020000);
+}
+__device__ inline int part_o_off(int db, int lane) { return (db * 64 + lane) * 16; }
+
+// Position on the tile line: tile t of segment (b, g); lb valid rows and nt tiles in sequence b,
+// pb the line position of sequence b's first segment.  All fields are wave-uniform.
+struct LineCursor {
+    int b, g, t, lb, nt;
+    long long pb;
+    __device__ inline int seg(int Hkv) const { return b * Hkv + g; }
+    // move to the next segment of the line (the caller knows there is one)
+    __device__ inline void next_segment(const DecodeArgs& a, const int* __restrict__ kv_len, int TR) {
+        t = 0;
+        if (++g == a.Hkv) {
+            g = 0;
+            pb += (long long)a.Hkv * nt;
+            ++b;
+            lb = valid_rows(a, kv_len, b);
+            nt = (lb + TR - 1) / TR;
+        }
+    }
+};
+
+// A piece whose segment other waves share: merged at the end of the share.
+struct PendingPiece {
+    int seg, npieces, wf;
+    long long ps;
+};
+
+template <int D, int TR, int NS, bool ROPE>
+__global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a, const int* __restrict__ kv_len) {
     constexpr int KB = TR / 16, KS = D / 32, DB = D / 16, K2 = TR / 32;
     using TC = TileCopy<D, 1, TR>;
     constexpr int kCopies = 2 * TC::NU;          // copies per tile (K~ and V)
@@ -354,7 +420,7 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
     // ---- this wave's share of the tile line ----
     // tiles of sequence b0 + lane and their inclusive prefix over the chunk of 64 sequences
     auto chunk_tiles = [&](int b0, int& tl, int& incl) {
-        tl = b0 + lane < a.B ? (valid_rows(a, b0 + lane) + TR - 1) / TR : 0;
+        tl = b0 + lane < a.B ? (valid_rows(a, kv_len, b0 + lane) + TR - 1) / TR : 0;
         incl = wave_incl_scan(tl, lane);
     };
     int tl, incl;
@@ -368,27 +434,49 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
     total = uniform(total * a.Hkv);
     const long long lo = (long long)w * total / W, hi = (long long)(w + 1) * total / W;
     if (lo >= hi) return;
-    int b = 0;
-    long long pb = 0;                             // line position of sequence b's first segment
+    const int nsh = (int)(hi - lo);               // tiles in the share
+    LineCursor cur;
+    cur.b = 0;
+    cur.pb = 0;
     for (int b0 = 0;; b0 += 64) {
         if (b0 > 0) chunk_tiles(b0, tl, incl);
-        const unsigned long long m = __builtin_amdgcn_ballot_w64(b0 + lane < a.B && pb + (long long)a.Hkv * incl > lo);
+        const unsigned long long m =
+            __builtin_amdgcn_ballot_w64(b0 + lane < a.B && cur.pb + (long long)a.Hkv * incl > lo);
         if (m) {
             const int f = __builtin_ctzll(m);
-            b = b0 + f;
-            pb += (long long)a.Hkv * (__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(tl, f));
+            cur.b = b0 + f;
+            cur.pb += (long long)a.Hkv * (__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(tl, f));
             break;
         }
-        pb += (long long)a.Hkv * __builtin_amdgcn_readlane(incl, 63);
+        cur.pb += (long long)a.Hkv * __builtin_amdgcn_readlane(incl, 63);
     }
-    b = uniform(b);
-    pb = uniform(pb);
-    int lb = valid_rows(a, b), nt_b = (lb + TR - 1) / TR;
-    int g = (int)((lo - pb) / nt_b), t0 = (int)((lo - pb) % nt_b);
+    cur.b = uniform(cur.b);
+    cur.pb = uniform(cur.pb);
+    cur.lb = valid_rows(a, kv_len, cur.b);
+    cur.nt = (cur.lb + TR - 1) / TR;
+    cur.g = (int)((lo - cur.pb) / cur.nt);
+    cur.t = (int)((lo - cur.pb) % cur.nt);
 
+    // ---- one copy stream over the whole share, NS - 1 tiles ahead of the computation ----
     const unsigned lk = lds_addr(&S.k[0][0]), lv = lds_addr(&S.v[0][0]);
     TC tc;
     tc.init(0, lane);
+    LineCursor icur = cur;                        // the next tile to fetch
+    auto issue_next = [&](int i) {                // share tile i, at icur
+        const size_t hoff = (size_t)icur.seg(a.Hkv) * a.Tc * D;
+        const unsigned hbytes = (unsigned)icur.lb * (unsigned)(D * 2);
+        const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.kc) + hoff, hbytes);
+        const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.vc) + hoff, hbytes);
+        const unsigned row0 = (unsigned)(icur.t * TR) * (unsigned)(D * 2);
+        const unsigned so = (unsigned)(i % NS) * TC::kBytes;
+        tc.copy(rk, row0, lk + so, 0);
+        tc.copy(rv, row0, lv + so, 0);
+        if (i + 1 < nsh && ++icur.t == icur.nt) icur.next_segment(a, kv_len, TR);
+    };
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nsh) issue_next(i);
+
     int roff[KB][KS], voff[K2][2][DB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -407,41 +495,33 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
     // never stored)
     const int cc = c < ncol ? c : 0;
     const int hh = cc / a.n, ti = cc % a.n;
+    auto out_row = [&](int b, int g) { return ((size_t)b * a.Hq + g * G + hh) * a.n + ti; };
 
-    for (long long x = lo;;) {
-        // ---- piece: tiles [t0, t1) of segment (b, g) ----
-        const int t1 = (int)min((long long)nt_b, t0 + (hi - x));
-        const int seg = b * a.Hkv + g;
-        const int k0 = t0 * TR, k1 = min(t1 * TR, lb), nt = t1 - t0;
-        const unsigned hbytes = (unsigned)lb * (unsigned)(D * 2);
-        const size_t hoff = (size_t)seg * a.Tc * D;
-        const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.kc) + hoff, hbytes);
-        const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.vc) + hoff, hbytes);
-        auto issue = [&](int i) {
-            const unsigned row0 = (unsigned)(k0 + i * TR) * (unsigned)(D * 2);
-            const unsigned so = (unsigned)(i % NS) * TC::kBytes;
-            tc.copy(rk, row0, lk + so, 0);
-            tc.copy(rv, row0, lv + so, 0);
-        };
-#pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-            if (i < nt) issue(i);
+    PendingPiece pend[2];
+    int npend = 0;
+    for (int i = 0;;) {
+        // ---- piece: tiles [cur.t, t1) of segment (cur.b, cur.g) ----
+        const int t1 = min(cur.nt, cur.t + (nsh - i));
+        const int seg = cur.seg(a.Hkv);
+        const int lb = cur.lb, k1 = min(t1 * TR, lb);
         const int pos = lb - a.n + ti;
         bf16x8 qhi[KS], qlo[KS];
-        q_operands16<D>(reinterpret_cast<const bf16*>(a.q) + (((size_t)b * a.Hq + g * G + hh) * a.n + ti) * D, cs, pos,
-                        g4, qhi, qlo);
-        wait_vmcnt<0>();   // query operands and the first tiles (see copy16_to_lds)
+        q_operands16<D, ROPE>(reinterpret_cast<const bf16*>(a.q) + out_row(cur.b, cur.g) * D, cs, pos, g4, qhi, qlo);
+        // The compiler waits for these loads with vmcnt(0) (it does not count the copies): pin the
+        // operands here so that the wait comes before the next copy is issued, not after it.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qhi[ks]), "+v"(qlo[ks]));
 
         f32x4 oacc[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
         float m_run = -INFINITY, l_run = 0.f;
 
-        for (int i = 0; i < nt; ++i) {
-            wait_tiles<kCopies, NS - 2>(nt - 1 - i);
-            if (i + NS - 1 < nt) issue(i + NS - 1);   // its stage was last read in step i - 1
+        for (int t = cur.t; t < t1; ++t, ++i) {
+            wait_tiles<kCopies, NS - 2>(nsh - 1 - i);
+            if (i + NS - 1 < nsh) issue_next(i + NS - 1);   // its stage was last read in step i - 1
             const int buf = i % NS;
-            const int j0 = k0 + i * TR;
+            const int j0 = t * TR;
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
             bf16x8 kf[KB][KS];
@@ -517,16 +597,16 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
             l_run += ls;
         }
 
-        // ---- the piece's result ----
+        // ---- the piece's result: final when the piece is its whole segment, else a partial ----
         const float l_tot = col_sum(l_run);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float L = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-        const long long ps = pb + (long long)g * nt_b;                // the segment on the line
-        const int wf = wave_of(ps, total, W), wl = wave_of(ps + nt_b - 1, total, W);
-        const int npieces = total >= W ? wl - wf + 1 : nt_b;         // waves holding part of it
-        const size_t orow = ((size_t)b * a.Hq + g * G + hh) * a.n + ti;
+        const long long ps = cur.pb + (long long)cur.g * cur.nt;    // the segment on the line
+        const int wf = wave_of(ps, total, W), wl = wave_of(ps + cur.nt - 1, total, W);
+        const int npieces = total >= W ? wl - wf + 1 : cur.nt;     // waves holding part of it
         if (npieces == 1) {
             if (c < ncol) {
+                const size_t orow = out_row(cur.b, cur.g);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const float y[4] = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
@@ -535,71 +615,95 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a) {
                 if (g4 == 0) a.lse[orow] = L;
             }
         } else {
-            // Partial results cross waves (and XCDs, whose L2 caches are not coherent with each
-            // other) through device-scope atomic stores and loads, which are coherent at that
-            // scope without the L2 write-back and invalidation of a device-scope fence: the
-            // stores complete (vmcnt 0) before the arrival count is raised, and the last arrival
-            // issues its loads only once the count has come back.
             const size_t slot = (size_t)w + seg;
-            float* __restrict__ po = a.part_o + (slot * 16 + c) * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __hip_atomic_store(po + 16 * db + 4 * g4 + e, oacc[db][e] * inv, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (g4 == 0) __hip_atomic_store(a.part_l + slot * 16 + c, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_vmcnt<0>();
-            int old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(a.ctr + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = uniform(old);                        // lane 0's value
-            if (old == npieces - 1) {                  // the last piece of the segment: merge
-                auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-                // the waves holding the pieces, in line order: wf .. wl when no share is empty,
-                // else one wave per tile
-                const bool dense = total >= W;
-                const int np = npieces;
-                auto piece_wave = [&](int k) { return dense ? wf + k : wave_of(ps + k, total, W); };
-                float mx = -INFINITY;
-                for (int k = 0; k < np; ++k) mx = fmaxf(mx, ld(a.part_l + ((size_t)piece_wave(k) + seg) * 16 + c));
-                float sum = 0.f;
-                f32x4 acc[DB];
-#pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
-                for (int k = 0; k < np; ++k) {
-                    const size_t sl = (size_t)piece_wave(k) + seg;
-                    const float lv_ = ld(a.part_l + sl * 16 + c);
-                    const float wt = lv_ == -INFINITY ? 0.f : __expf(lv_ - mx);   // mx is finite: key 0 is seen
-                    sum += wt;
-                    const float* pv = a.part_o + (sl * 16 + c) * D;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[db][e] += wt * ld(pv + 16 * db + 4 * g4 + e);
-                }
-                if (c < ncol) {
-                    const float is = 1.f / sum;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const float y[4] = {acc[db][0] * is, acc[db][1] * is, acc[db][2] * is, acc[db][3] * is};
-                        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + orow * D + 16 * db + 4 * g4) = cvt4(y);
-                    }
-                    if (g4 == 0) a.lse[orow] = mx + __logf(sum);
-                }
-                if (lane == 0) __hip_atomic_store(a.ctr + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int db = 0; db < DB; ++db) {
+                const f32x4 y = oacc[db] * inv;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), part_o_rsrc<D>(a, slot),
+                                                       part_o_off(db, lane), 0, kDeviceScope);
             }
+            if (g4 == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), part_l_rsrc(a, slot), 4 * c, 0, kDeviceScope);
+            // only the first and the last piece of a share can share their segment with others
+            const PendingPiece pp{seg, npieces, wf, ps};
+            if (npend == 0) pend[0] = pp;
+            else pend[1] = pp;
+            ++npend;
         }
+        if (i >= nsh) break;
+        cur.next_segment(a, kv_len, TR);
+    }
 
-        x += nt;
-        if (x >= hi) break;
-        t0 = 0;
-        if (++g == a.Hkv) {
-            g = 0;
-            pb += (long long)a.Hkv * nt_b;
-            ++b;
-            lb = valid_rows(a, b);
-            nt_b = (lb + TR - 1) / TR;
+    // ---- pieces of shared segments: count the arrival; the last one merges ----
+    // The partial stores complete (vmcnt 0) before the count is raised, and the last arrival
+    // issues its loads only once the count has come back.
+    wait_vmcnt<0>();
+    int arrived[2] = {0, 0};                     // both counts raised before either is looked at
+    if (lane == 0) {
+        if (npend > 0) arrived[0] = __hip_atomic_fetch_add(a.ctr + pend[0].seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (npend > 1) arrived[1] = __hip_atomic_fetch_add(a.ctr + pend[1].seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    arrived[0] = uniform(arrived[0]);            // lane 0's values
+    arrived[1] = uniform(arrived[1]);
+    for (int k = 0; k < npend; ++k) {
+        const PendingPiece pp = k == 0 ? pend[0] : pend[1];
+        if ((k == 0 ? arrived[0] : arrived[1]) != pp.npieces - 1) continue;
+        asm volatile("" ::: "memory");           // the loads below stay after the count
+        // the waves holding the pieces, in line order: wf .. wf + npieces - 1 when no share is
+        // empty, else one wave per tile
+        const bool dense = total >= W;
+        auto piece_wave = [&](int q) { return dense ? pp.wf + q : wave_of(pp.ps + q, total, W); };
+        // running log-sum-exp over batches of kMergeBatch pieces, every load of a batch issued
+        // before any is used (a batch past the last piece re-reads it with weight 0)
+        constexpr int kMergeBatch = kDecodeMergeBatch;
+        float mx = -INFINITY, sum = 0.f;
+        f32x4 acc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+        for (int q0 = 0; q0 < pp.npieces; q0 += kMergeBatch) {
+            float lq[kMergeBatch];
+            f32x4 ov[kMergeBatch][DB];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const size_t sl = (size_t)piece_wave(min(q0 + u, pp.npieces - 1)) + pp.seg;
+                lq[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_l_rsrc(a, sl), 4 * c, 0, kDeviceScope));
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    ov[u][db] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              part_o_rsrc<D>(a, sl), part_o_off(db, lane), 0, kDeviceScope));
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+                if (q0 + u >= pp.npieces) lq[u] = -INFINITY;
+            float bm = lq[0];
+#pragma unroll
+            for (int u = 1; u < kMergeBatch; ++u) bm = fmaxf(bm, lq[u]);
+            const float m_new = fmaxf(mx, bm);
+            if (m_new == -INFINITY) continue;          // no piece so far saw a key of this column
+            const float sc = mx == -INFINITY ? 0.f : __expf(mx - m_new);
+            sum *= sc;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= sc;
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float wt = lq[u] == -INFINITY ? 0.f : __expf(lq[u] - m_new);
+                sum += wt;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] += wt * ov[u][db];
+            }
+            mx = m_new;
         }
+        if (c < ncol) {
+            const size_t orow = out_row(pp.seg / a.Hkv, pp.seg % a.Hkv);
+            const float is = 1.f / sum;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const float y[4] = {acc[db][0] * is, acc[db][1] * is, acc[db][2] * is, acc[db][3] * is};
+                *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + orow * D + 16 * db + 4 * g4) = cvt4(y);
+            }
+            if (g4 == 0) a.lse[orow] = mx + __logf(sum);
+        }
+        if (lane == 0) __hip_atomic_store(a.ctr + pp.seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -629,7 +733,7 @@ int decode16_slots() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode16_kernel<D, kDecodeTileRows, kDecodeStages>), 64, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&decode16_kernel<D, kDecodeTileRows, kDecodeStages, true>), 64, 0) !=
         hipSuccess)
         return 0;
     const int v = std::max(1, cus * per_cu);
@@ -639,8 +743,12 @@ int decode16_slots() {
 
 template <int D>
 hipError_t launch_decode16(const DecodeArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages>), dim3((unsigned)a.nsplit), dim3(64), 0,
-                       stream, a);
+    if (a.rope_cs)
+        hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages, true>), dim3((unsigned)a.nsplit), dim3(64),
+                           0, stream, a, a.kv_len);
+    else
+        hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages, false>), dim3((unsigned)a.nsplit),
+                           dim3(64), 0, stream, a, a.kv_len);
     return hipGetLastError();
 }
 

@@ -64,6 +64,7 @@ struct DecodeArgs {
 constexpr int kDecodeTileRows = 64;
 constexpr int kDecodeStages = 3;
 constexpr int kDecodeMaxWaves = 4096;
+constexpr int kDecodeMergeBatch = 8;      // pieces merged per round of loads
 
 struct RopeArgs {
     const void* x;
