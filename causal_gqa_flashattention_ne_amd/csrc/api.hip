@@ -22,8 +22,9 @@ int check_attn(const ne_attn_params* p) {
     if (!p) return NE_ERR_NULL;
     if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->T <= 0 || p->D <= 0) return NE_ERR_SHAPE;
     if (p->Hq % p->Hkv != 0) return NE_ERR_SHAPE;
-    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
     if (p->dtype != NE_DTYPE_F32 && p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
+    // head_dim 32 or 64; 128 on the bf16 path only (the fp32 tiles would not fit in LDS)
+    if (p->D != 32 && p->D != 64 && !(p->D == 128 && p->dtype == NE_DTYPE_BF16)) return NE_ERR_UNSUPPORTED;
     if (p->causal != 1) return NE_ERR_UNSUPPORTED;
     if ((long)p->B * p->Hq * p->T * p->D > kMaxElems) return NE_ERR_SHAPE;
     if (!isfinite(p->scale)) return NE_ERR_SHAPE;
@@ -54,12 +55,26 @@ size_t delta_bytes(const ne_attn_params* p) {
     return (n + 255) & ~(size_t)255;
 }
 
+// the attention kernels: bf16 with D in {32, 64, 128}, fp32 with D in {32, 64}
 template <typename F>
 int dispatch(int dtype, int D, F&& f) {
     hipError_t e;
-    if (dtype == NE_DTYPE_BF16) e = D == 64 ? f(ne::bf16{}, std::integral_constant<int, 64>{})
-                                            : f(ne::bf16{}, std::integral_constant<int, 32>{});
+    if (dtype == NE_DTYPE_BF16)
+        e = D == 128  ? f(ne::bf16{}, std::integral_constant<int, 128>{})
+            : D == 64 ? f(ne::bf16{}, std::integral_constant<int, 64>{})
+                      : f(ne::bf16{}, std::integral_constant<int, 32>{});
     else e = D == 64 ? f(float{}, std::integral_constant<int, 64>{}) : f(float{}, std::integral_constant<int, 32>{});
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+// the RoPE kernels: either dtype with D in {32, 64, 128}
+template <typename F>
+int dispatch_rope(int dtype, int D, F&& f) {
+    auto by_d = [&](auto t) {
+        return D == 128 ? f(t, std::integral_constant<int, 128>{})
+               : D == 64 ? f(t, std::integral_constant<int, 64>{}) : f(t, std::integral_constant<int, 32>{});
+    };
+    const hipError_t e = dtype == NE_DTYPE_BF16 ? by_d(ne::bf16{}) : by_d(float{});
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
@@ -87,7 +102,7 @@ struct Decode16Layout {
     size_t ctr, part_l, part_o, total;
     explicit Decode16Layout(const ne_decode_params* p) {
         const long nseg = (long)p->B * p->Hkv;
-        max_tiles = nseg * ((p->cache_rows + ne::kDecodeTileRows - 1) / ne::kDecodeTileRows);
+        max_tiles = nseg * ((p->cache_rows + ne::decode_tile_rows(p->D) - 1) / ne::decode_tile_rows(p->D));
         wcap = (int)std::min<long>(ne::kDecodeMaxWaves, max_tiles);
         const size_t slots = (size_t)wcap + nseg;
         ctr = 0;
@@ -99,16 +114,17 @@ struct Decode16Layout {
 
 // Waves of the 16-column grid (never more than fit at once): the fewest that minimise the
 // estimated time with every cache full, a wave's tiles (one step each) plus the merge of a
-// segment's pieces (one round of loads, costed like a step, per kDecodeMergeBatch pieces).
+// segment's pieces (one round of loads, costed like a step, per merge batch of pieces).
 // Scans the tiles per wave k upward from the smallest feasible one; the cost is at least k.
 long decode16_waves(const ne_decode_params* p, const Decode16Layout& L, int slots) {
-    const long seg_tiles = (p->cache_rows + ne::kDecodeTileRows - 1) / ne::kDecodeTileRows;
+    const long seg_tiles = (p->cache_rows + ne::decode_tile_rows(p->D) - 1) / ne::decode_tile_rows(p->D);
     const long wmax = std::max<long>(1, std::min<long>(L.wcap, slots));
     long best = 1, best_cost = -1;
     for (long k = (L.max_tiles + wmax - 1) / wmax; best_cost < 0 || k <= best_cost; ++k) {
         const long w = (L.max_tiles + k - 1) / k;                       // fewest waves with <= k tiles
         const long pieces = k >= seg_tiles ? 1 : (seg_tiles + k - 1) / k + 1;
-        const long cost = k + (pieces > 1 ? (pieces + ne::kDecodeMergeBatch - 1) / ne::kDecodeMergeBatch : 0);
+        const long mb = ne::decode_merge_batch(p->D);
+        const long cost = k + (pieces > 1 ? (pieces + mb - 1) / mb : 0);
         if (best_cost < 0 || cost <= best_cost) best = w, best_cost = cost;   // ties: fewer waves
     }
     return best;
@@ -119,9 +135,10 @@ int check_decode(const ne_decode_params* p) {
     if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->n <= 0 || p->D <= 0 || p->cache_rows <= 0)
         return NE_ERR_SHAPE;
     if (p->Hq % p->Hkv != 0 || p->n > p->cache_rows) return NE_ERR_SHAPE;
-    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
+    if (p->D != 32 && p->D != 64 && p->D != 128) return NE_ERR_UNSUPPORTED;
     if (p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
     if ((long)(p->Hq / p->Hkv) * p->n > 32) return NE_ERR_UNSUPPORTED;
+    if (p->D == 128 && (long)(p->Hq / p->Hkv) * p->n > 16) return NE_ERR_UNSUPPORTED;   // 16-column path only
     if ((long)p->B * p->Hkv * p->cache_rows * p->D > kMaxElems) return NE_ERR_SHAPE;
     if ((long)p->B * p->Hq * p->n * p->D > kMaxElems) return NE_ERR_SHAPE;
     if (!isfinite(p->scale)) return NE_ERR_SHAPE;
@@ -163,14 +180,14 @@ int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream
 int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream) {
     if (!p) return NE_ERR_NULL;
     if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->D <= 0 || p->pos_offset < 0) return NE_ERR_SHAPE;
-    if (p->D != 32 && p->D != 64) return NE_ERR_UNSUPPORTED;
+    if (p->D != 32 && p->D != 64 && p->D != 128) return NE_ERR_UNSUPPORTED;
     if (p->dtype != NE_DTYPE_F32 && p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
     if ((long)p->B * p->H * p->T * p->D > kMaxElems) return NE_ERR_SHAPE;
     if ((long)p->T + p->pos_offset > p->rope_rows) return NE_ERR_SHAPE;
     if (int rc = check_ptrs({x, y, p->rope_cs})) return rc;
     ne::RopeArgs a{x, y, p->rope_cs, p->B * p->H * p->T, p->T, p->pos_offset, inverse};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+    return dispatch_rope(p->dtype, p->D, [&](auto t, auto d) {
         return ne::launch_rope<decltype(t), decltype(d)::value>(a, s);
     });
 }
@@ -232,14 +249,16 @@ int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache
     hipError_t e;
     if (decode_narrow(p)) {
         const Decode16Layout L(p);
-        const int slots = p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
+        const int slots = p->D == 128 ? ne::decode16_slots<128>()
+                          : p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
         if (slots <= 0) return NE_ERR_HIP;
         const long waves = decode16_waves(p, L, slots);
         ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse,
                          reinterpret_cast<float*>(ws + L.part_o), reinterpret_cast<float*>(ws + L.part_l),
                          reinterpret_cast<int*>(ws + L.ctr), p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows,
                          (int)std::max<long>(1, waves), 0, scale};
-        e = p->D == 64 ? ne::launch_decode16<64>(a, s) : ne::launch_decode16<32>(a, s);
+        e = p->D == 128 ? ne::launch_decode16<128>(a, s)
+            : p->D == 64 ? ne::launch_decode16<64>(a, s) : ne::launch_decode16<32>(a, s);
     } else {
         int nsplit, chunk;
         decode_split(p, &nsplit, &chunk);

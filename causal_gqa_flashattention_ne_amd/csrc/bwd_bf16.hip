@@ -548,8 +548,10 @@ hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template hipError_t launch_bwd_pre_bf16<128>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre_bf16<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre_bf16<32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_main_bf16<128>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main_bf16<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main_bf16<32>(const BwdArgs&, hipStream_t);
 

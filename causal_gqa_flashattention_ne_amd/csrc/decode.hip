@@ -655,7 +655,7 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a, const int* _
         auto piece_wave = [&](int q) { return dense ? pp.wf + q : wave_of(pp.ps + q, total, W); };
         // running log-sum-exp over batches of kMergeBatch pieces, every load of a batch issued
         // before any is used (a batch past the last piece re-reads it with weight 0)
-        constexpr int kMergeBatch = kDecodeMergeBatch;
+        constexpr int kMergeBatch = decode_merge_batch(D);
         float mx = -INFINITY, sum = 0.f;
         f32x4 acc[DB];
 #pragma unroll
@@ -733,7 +733,7 @@ int decode16_slots() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode16_kernel<D, kDecodeTileRows, kDecodeStages, true>), 64, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&decode16_kernel<D, decode_tile_rows(D), kDecodeStages, true>), 64, 0) !=
         hipSuccess)
         return 0;
     const int v = std::max(1, cus * per_cu);
@@ -744,16 +744,18 @@ int decode16_slots() {
 template <int D>
 hipError_t launch_decode16(const DecodeArgs& a, hipStream_t stream) {
     if (a.rope_cs)
-        hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages, true>), dim3((unsigned)a.nsplit), dim3(64),
+        hipLaunchKernelGGL((decode16_kernel<D, decode_tile_rows(D), kDecodeStages, true>), dim3((unsigned)a.nsplit), dim3(64),
                            0, stream, a, a.kv_len);
     else
-        hipLaunchKernelGGL((decode16_kernel<D, kDecodeTileRows, kDecodeStages, false>), dim3((unsigned)a.nsplit),
+        hipLaunchKernelGGL((decode16_kernel<D, decode_tile_rows(D), kDecodeStages, false>), dim3((unsigned)a.nsplit),
                            dim3(64), 0, stream, a, a.kv_len);
     return hipGetLastError();
 }
 
+template int decode16_slots<128>();
 template int decode16_slots<64>();
 template int decode16_slots<32>();
+template hipError_t launch_decode16<128>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode16<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode16<32>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode<64>(const DecodeArgs&, hipStream_t);

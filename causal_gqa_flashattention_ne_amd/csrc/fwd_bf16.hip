@@ -237,6 +237,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template hipError_t launch_fwd_bf16<128>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_bf16<64>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_bf16<32>(const FwdArgs&, hipStream_t);
 

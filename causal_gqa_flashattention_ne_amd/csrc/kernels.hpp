@@ -60,11 +60,12 @@ struct DecodeArgs {
     float scale;
 };
 
-// 16-column decode path: keys per staged tile, LDS stages, and the cap on the grid's waves
-constexpr int kDecodeTileRows = 64;
+// 16-column decode path: keys per staged tile (32 at D = 128, so that three stages stay at
+// 48 KiB of LDS), LDS stages, the cap on the grid's waves, pieces merged per round of loads
+constexpr int decode_tile_rows(int D) { return D == 128 ? 32 : 64; }
 constexpr int kDecodeStages = 3;
 constexpr int kDecodeMaxWaves = 4096;
-constexpr int kDecodeMergeBatch = 8;      // pieces merged per round of loads
+constexpr int decode_merge_batch(int D) { return D == 128 ? 4 : 8; }
 
 struct RopeArgs {
     const void* x;

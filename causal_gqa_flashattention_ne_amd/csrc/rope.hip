@@ -58,6 +58,8 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template hipError_t launch_rope<bf16, 128>(const RopeArgs&, hipStream_t);
+template hipError_t launch_rope<float, 128>(const RopeArgs&, hipStream_t);
 template hipError_t launch_rope<bf16, 64>(const RopeArgs&, hipStream_t);
 template hipError_t launch_rope<bf16, 32>(const RopeArgs&, hipStream_t);
 template hipError_t launch_rope<float, 64>(const RopeArgs&, hipStream_t);

@@ -149,6 +149,8 @@ WORKLOADS = {
     4: Workload("gpt116m-stack-bf16-x16", 16, 12, 4, 512, 64, "bf16", layers=16, sigma_do=0.1, seed=4),
     5: Workload("byte-mha-bf16-t2048", 8, 8, 8, 2048, 64, "bf16", outlier_frac=0.01,
                 outlier_scale=8.0, seed=5),
+    # head_dim 128 variant of the 116M layer: the same width (768) as 6 query heads over 2 kv heads
+    6: Workload("gpt116m-width-d128-bf16", 16, 6, 2, 512, 128, "bf16", sigma_do=0.1, seed=6),
 }
 
 

@@ -63,7 +63,8 @@ def bwd(p, ws_bytes=1 << 30, ptrs=None):
     (dict(T=-1), -2),
     (dict(Hkv=0), -2),
     (dict(D=48), -3),
-    (dict(D=128), -3),
+    (dict(D=256), -3),
+    (dict(D=128, dtype_code=ne.NE_DTYPE_F32), -3),   # head_dim 128 on the bf16 path only
     (dict(dtype_code=7), -3),
     (dict(B=1 << 20, Hq=64, Hkv=1, T=1 << 10), -2),
 ])
@@ -167,12 +168,21 @@ def dec(p, ws_bytes=1 << 30, ptrs=None):
     (dict(n=200), -2),                      # more new tokens than cache rows
     (dict(D=48), -3),
     (dict(n=17), -3),                       # G * n = 34 > 32 query columns
+    (dict(D=128, n=9), -3),                 # head_dim 128: at most 16 query columns
+    (dict(D=256), -3),
     (dict(cache_rows=1 << 26), -2),
 ])
 def test_decode_rejects_bad_shapes(kw, code):
     p = dparams(**kw)
     assert dec(p) == code
     assert ne.lib().ne_attn_decode_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_head_dim_128_accepted():
+    pb = params(D=128, dtype_code=ne.NE_DTYPE_BF16)
+    assert ne.lib().ne_attn_bwd_workspace_bytes(ctypes.byref(pb)) > 0
+    assert ne.decode_workspace_bytes(dparams(D=128, n=8)) > 0      # G * n = 16
+    assert ne.decode_workspace_bytes(dparams(D=64, n=9)) > 0       # 18 columns: the 32-column path
 
 
 def test_decode_dtype_pointers_workspace():

@@ -60,6 +60,8 @@ CASES = [
     (12, 1, 3, 1, 5, 130, 64, [65]),           # a last piece no column of the first tokens sees
     (13, 3, 16, 1, 1, 700, 64, [700, 1, 333]), # G = 16: the widest 16-column group
     (14, 2, 8, 2, 2, 1000, 64, [100, 200]),    # fewer valid tiles than waves: one-tile shares
+    (15, 3, 6, 2, 1, 1000, 128, None),         # head_dim 128 (32-key tiles)
+    (16, 2, 4, 1, 4, 300, 128, [300, 9]),      # head_dim 128, 16 columns, short sequence
 ]
 
 
