@@ -47,7 +47,7 @@ enum {
     NE_OK = 0,
     NE_ERR_NULL = -1,        /* a required pointer is NULL */
     NE_ERR_SHAPE = -2,       /* a size <= 0, Hq % Hkv != 0, rope table too short, ... */
-    NE_ERR_UNSUPPORTED = -3, /* head_dim not in {32, 64}, unknown dtype, causal != 1 */
+    NE_ERR_UNSUPPORTED = -3, /* head_dim not supported (see each call), unknown dtype, causal != 1 */
     NE_ERR_ALIGN = -4,       /* a pointer that is not 16-byte aligned */
     NE_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure */
     NE_ERR_HIP = -6          /* the HIP runtime reported an error on launch */
@@ -56,7 +56,8 @@ enum {
 enum { NE_DTYPE_F32 = 0, NE_DTYPE_BF16 = 1 };
 
 typedef struct ne_attn_params {
-    int32_t B, Hq, Hkv, T, D;   /* batch, query heads, kv heads, sequence length, head_dim */
+    int32_t B, Hq, Hkv, T, D;   /* batch, query heads, kv heads, sequence length, head_dim:
+                                   32 or 64, or 128 with NE_DTYPE_BF16 */
     int32_t dtype;              /* NE_DTYPE_F32 or NE_DTYPE_BF16 */
     int32_t causal;             /* must be 1 */
     float scale;                /* softmax scale; <= 0 means 1/sqrt(D) */
@@ -89,7 +90,7 @@ int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream
 /*
  * y = R x (inverse == 0) or y = R^T x (inverse != 0) for x, y of shape [B, H, T, D] in dtype;
  * row t uses the table row t + pos_offset.  x == y (in place) is allowed; other overlap is not.
- * D must be in {32, 64}.  (Rotary embedding of queries and keys: agentlenshq NanoEuler page,
+ * D must be in {32, 64, 128}.  (Rotary embedding of queries and keys: agentlenshq NanoEuler page,
  * "기술 사양"; byte-level GPT page, "Core Mechanics".)
  */
 int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream);
@@ -166,8 +167,8 @@ int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, cons
  *            It must be zero-filled before its first use; every call leaves it ready for the
  *            next one (arrival counters back at zero).  Calls that share a workspace must not
  *            overlap in time.
- * bf16 only; D in {32, 64}; (Hq/Hkv) * n <= 32 (the query columns of one kv group share its key
- * tiles).  With (Hq/Hkv) * n <= 16: one launch on stream; the valid tiles of all (sequence, kv
+ * bf16 only; D in {32, 64, 128}; (Hq/Hkv) * n <= 32 (the query columns of one kv group share its
+ * key tiles), <= 16 when D = 128.  With (Hq/Hkv) * n <= 16: one launch on stream; the valid tiles of all (sequence, kv
  * head) pairs are split evenly over the waves that fit on the device, and the pieces of a pair
  * are merged by log-sum-exp inside the launch.  Otherwise two launches (fixed key chunks, then
  * the merge).  Returns NE_ERR_HIP if the device cannot be queried or a launch fails.
