@@ -32,7 +32,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "pick": 4, "len": 5}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "pick": 4, "len": 5, "x": 6, "w": 7}
 
 
 def mix64(z):
@@ -221,3 +221,35 @@ def decode_inputs(w: DecodeWorkload):
     """(q, k, v, kv_len) of decode workload w (k un-rotated; the caller rotates it into the cache)."""
     return decode_case(w.seed, w.B, w.Hq, w.Hkv, w.n, w.cache_rows, w.D,
                        [w.cache_rows] * w.B if w.full else None)
+
+
+def qkv_case(seed, B, T, C, Hq, Hkv, D, dtype="bf16"):
+    """Inputs of the query/key/value projection: activations x [B, T, C] ~ N(0, 1) (the unit-RMS
+    output of the pre-norm) and packed weights w [(Hq + 2 Hkv) D, C] ~ N(0, 1/C), so that every
+    projected feature has unit variance."""
+    x = tensor(seed, 0, "x", (B, T, C), 1.0, dtype)
+    w = tensor(seed, 0, "w", ((Hq + 2 * Hkv) * D, C), 1.0 / np.sqrt(C), dtype)
+    return x, w
+
+
+@dataclasses.dataclass(frozen=True)
+class QkvWorkload:
+    name: str
+    B: int
+    T: int
+    C: int
+    Hq: int
+    Hkv: int
+    D: int
+    theta: float = 10000.0
+    seed: int = 0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.B * self.T * self.C * (self.Hq + 2 * self.Hkv) * self.D
+
+
+# The 116M model's projection: 16 sequences of 512 tokens, width 768, 12 query and 4 kv heads of 64
+QKV_WORKLOADS = {
+    1: QkvWorkload("gpt116m-qkv-proj-bf16", 16, 512, 768, 12, 4, 64, seed=21),
+}

@@ -148,3 +148,27 @@ def decode(q, k_cache, v_cache, kv_len, theta=10000.0, scale=None):
             o[b, h] = (e / l) @ V
             L[b, h] = (m + np.log(l))[:, 0]
     return o, L
+
+
+def qkv_proj(x, w, Hq, Hkv, theta=10000.0):
+    """The query, key and value projections of one attention block, in double, with RoPE on the
+    queries and keys (bias-free linear maps: agentlenshq NanoEuler page, "핵심 아키텍처 및 설계";
+    RoPE on queries and keys: "기술 사양").
+
+    x [B, T, C]: the (normalised) activations.  w [(Hq + 2 Hkv) D, C]: the packed weights, output
+    feature f = x . w[f]; the features are [query heads | key heads | value heads], head-major with
+    d fastest inside each head.  Returns (q, k, v) in the attention layout [B, H, T, D]: q and k
+    rotated at positions 0 .. T-1 (theta <= 0: not rotated), v as projected.
+    """
+    x, w = _d(x), _d(w)
+    B, T, C = x.shape
+    N = w.shape[0]
+    if w.shape[1] != C or N % (Hq + 2 * Hkv):
+        raise ValueError("shape mismatch")
+    D = N // (Hq + 2 * Hkv)
+    y = x.reshape(B * T, C) @ w.T                          # [B*T, N]
+    y = y.reshape(B, T, Hq + 2 * Hkv, D).transpose(0, 2, 1, 3)
+    q, k, v = y[:, :Hq], y[:, Hq:Hq + Hkv], y[:, Hq + Hkv:]
+    if theta > 0:
+        q, k = rope(q, theta), rope(k, theta)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
