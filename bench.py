@@ -11,6 +11,10 @@ Prints ONE JSON line.  value = whole-job algorithmic TFLOP/s with the causal pai
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
 
+With --qkv 1, the step is one call of the query/key/value projection (ne_qkv_proj: x W^T with
+RoPE on queries and keys, written into the attention layout) on the 116M model's shapes, and
+value = its TFLOP/s (2 * B*T * C * (Hq + 2 Hkv) D per call).
+
 With --decode D, the step is instead one decode call (ne_attn_decode: n new tokens per sequence
 against a rotated bf16 KV cache, split over the key range and merged) on decode workload D, and
 value = algorithmic HBM GB/s of that call (cache rows read once, queries read, outputs written).
@@ -37,6 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
     ap.add_argument("--decode", type=int, default=0, help="decode workload id 1..2 instead of the training step")
+    ap.add_argument("--qkv", type=int, default=0, help="projection workload id (1) instead of the training step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -93,6 +98,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.decode:
         return bench_decode(args, dev)
+    if args.qkv:
+        return bench_qkv(args, dev)
     w = gen.WORKLOADS[args.workload]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4
@@ -246,6 +253,97 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
     return {"kernel": "torch.neg (elementwise)", "read_bytes": src.numel() * 2, "write_bytes": dst.numel() * 2,
             "launches": 5}
+
+
+def bench_qkv(args, dev):
+    import torch
+
+    import causal_gqa_flashattention_ne_amd as ne
+    import gen
+
+    w = gen.QKV_WORKLOADS[args.qkv]
+    x, wt = gen.qkv_case(w.seed, w.B, w.T, w.C, w.Hq, w.Hkv, w.D)
+    xd = torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+    wd = torch.from_numpy(wt).to(dev).to(torch.bfloat16).contiguous()
+    cs = ne.rope_table(w.T, w.D, w.theta, dev)
+    p = ne.make_qkv_params(w.B, w.T, w.C, w.Hq, w.Hkv, w.D, cs)
+    q = torch.empty(w.B, w.Hq, w.T, w.D, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(w.B, w.Hkv, w.T, w.D, dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    stream = torch.cuda.current_stream(dev)
+    st = ne.ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        ne.qkv_proj_into(p, xd, wd, q, k, v, st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    avg_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flop = float(w.flops)
+    M, N = w.B * w.T, (w.Hq + 2 * w.Hkv) * w.D
+    nbytes = 2 * (M * w.C + N * w.C + M * N)         # x, w read once; q, k, v written once
+    peak = PEAK_TFLOPS["bf16"]
+    roof = {"bound": "mfma", "achieved": flop / (avg_us * 1e-6) / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    if nbytes / (PEAK_HBM_GBS * 1e9) > flop / (peak * 1e12):
+        roof = {"bound": "hbm", "achieved": nbytes / (avg_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name, "qkv_proj")
+    roof.update({"kernel": "qkv_proj", "avg_us": avg_us, "algorithmic_flop": flop, "algorithmic_bytes": nbytes})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        with threadpool_limits(limits=threads):
+            t_s = time.perf_counter()
+            passes = 0
+            while True:               # the whole projection in double, repeated for >= 2 s
+                oracle.qkv_proj(x, wt, w.Hq, w.Hkv, theta=w.theta)
+                passes += 1
+                if time.perf_counter() - t_s >= 2.0:
+                    break
+            dt = time.perf_counter() - t_s
+        cpu = {"value": flop * passes / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": "the whole projection in double (numpy matmul + RoPE) x %d passes, %.2f s wall"
+                         % (passes, dt)}
+
+    out = {
+        "metric": "query/key/value projection with RoPE epilogue, TFLOP/s",
+        "value": flop / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normals: x ~ N(0,1), w ~ N(0,1/C))",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "C": w.C, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "rope_theta": w.theta, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.copy_calibration:
+        out["copy_calibration"] = copy_calibration(dev)
+    print(json.dumps(out))
 
 
 def decode_bytes(w, lens):

@@ -27,11 +27,11 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
            "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main",
-           "ne_attn_decode_workspace_bytes", "ne_attn_decode")
+           "ne_attn_decode_workspace_bytes", "ne_attn_decode", "ne_qkv_proj")
 
 
 class AttnParams(ctypes.Structure):
@@ -46,6 +46,12 @@ class DecodeParams(ctypes.Structure):
                 ("n", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("cache_rows", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
+
+
+class QkvParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rope_cs", ctypes.c_void_p), ("rope_rows", ctypes.c_int32)]
 
 
 class RopeParams(ctypes.Structure):
@@ -88,8 +94,9 @@ def lib():
         L.ne_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
         L.ne_attn_decode_workspace_bytes.restype = sz
         L.ne_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 7 + [sz, vp]
+        L.ne_qkv_proj.argtypes = [ctypes.POINTER(QkvParams)] + [vp] * 6
         for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
-                  "ne_attn_bwd_main", "ne_attn_decode"):
+                  "ne_attn_bwd_main", "ne_attn_decode", "ne_qkv_proj"):
             getattr(L, f).restype = ctypes.c_int
         if L.ne_abi_version() != ABI_VERSION:
             raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
@@ -313,3 +320,39 @@ def attn_decode(q, k_cache, v_cache, kv_len, rope_theta: float = 10000.0, scale=
     ws = torch.zeros(max(1, decode_workspace_bytes(p)), dtype=torch.uint8, device=q.device)
     attn_decode_into(p, q, k_cache, v_cache, kv_len, o, lse, ws)
     return o, lse
+
+
+def make_qkv_params(B, T, C, Hq, Hkv, D, rope_cs=None) -> QkvParams:
+    p = QkvParams()
+    p.B, p.T, p.C, p.Hq, p.Hkv, p.D = B, T, C, Hq, Hkv, D
+    p.dtype = NE_DTYPE_BF16
+    p.rope_cs = rope_cs.data_ptr() if rope_cs is not None else None
+    p.rope_rows = rope_cs.shape[0] if rope_cs is not None else 0
+    return p
+
+
+def qkv_proj_into(p: QkvParams, x, w, q, k, v, stream=None):
+    """Projection into preallocated q, k, v ([B, H, T, D] bf16)."""
+    st = stream if stream is not None else _stream(x.device)
+    _check("ne_qkv_proj", lib().ne_qkv_proj(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), st))
+
+
+def qkv_proj(x, w, Hq: int, Hkv: int, rope_theta: float = 10000.0):
+    """Query, key and value projections with RoPE on queries and keys (bfloat16).
+
+    x [B, T, C]; w [(Hq + 2 Hkv) D, C], features packed [query heads | key heads | value heads].
+    Returns (q [B, Hq, T, D] rotated, k [B, Hkv, T, D] rotated, v [B, Hkv, T, D]).
+    """
+    _need(x, "x")
+    _need(w, "w", dtype=x.dtype, device=x.device)
+    if x.dim() != 3 or w.dim() != 2 or w.shape[1] != x.shape[2] or w.shape[0] % (Hq + 2 * Hkv):
+        raise ValueError("x must be [B, T, C] and w [(Hq + 2 Hkv) D, C]")
+    B, T, C = x.shape
+    D = w.shape[0] // (Hq + 2 * Hkv)
+    cs = rope_table(T, D, rope_theta, x.device) if rope_theta and rope_theta > 0 else None
+    p = make_qkv_params(B, T, C, Hq, Hkv, D, cs)
+    q = torch.empty((B, Hq, T, D), dtype=x.dtype, device=x.device)
+    k = torch.empty((B, Hkv, T, D), dtype=x.dtype, device=x.device)
+    v = torch.empty_like(k)
+    qkv_proj_into(p, x, w, q, k, v)
+    return q, k, v

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libne_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "fwd.hip", "fwd_bf16.hip", "bwd.hip", "bwd_bf16.hip", "rope.hip", "decode.hip"]
+SOURCES = ["api.hip", "fwd.hip", "fwd_bf16.hip", "bwd.hip", "bwd_bf16.hip", "rope.hip", "decode.hip", "proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

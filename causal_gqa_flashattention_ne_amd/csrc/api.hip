@@ -271,6 +271,28 @@ int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache
     return e == hipSuccess ? NE_OK : NE_ERR_HIP;
 }
 
+int ne_qkv_proj(const ne_qkv_params* p, const void* x, const void* w, void* q, void* k, void* v, void* stream) {
+    if (!p) return NE_ERR_NULL;
+    if (p->B <= 0 || p->T <= 0 || p->C <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0) return NE_ERR_SHAPE;
+    if (p->dtype != NE_DTYPE_BF16) return NE_ERR_UNSUPPORTED;
+    if (p->D != 32 && p->D != 64 && p->D != 128) return NE_ERR_UNSUPPORTED;
+    if (p->C % 64 != 0) return NE_ERR_UNSUPPORTED;
+    const long M = (long)p->B * p->T, N = (long)(p->Hq + 2L * p->Hkv) * p->D;
+    // byte offsets of whole tiles (rows past M or N included) stay below 2^32
+    const long pad = ne::proj_tile_tokens() > 128 ? ne::proj_tile_tokens() : 128;
+    if ((M + pad) * p->C > kMaxElems || (N + pad) * p->C > kMaxElems || M * N > kMaxElems) return NE_ERR_SHAPE;
+    if (p->rope_cs) {
+        if (p->rope_rows < p->T) return NE_ERR_SHAPE;
+        if (!aligned16(p->rope_cs)) return NE_ERR_ALIGN;
+    }
+    if (int rc = check_ptrs({x, w, q, k, v})) return rc;
+    const int tm = (int)((M + ne::proj_tile_tokens() - 1) / ne::proj_tile_tokens());
+    const int tn = (int)((N + 127) / 128);
+    ne::ProjArgs a{x, w, q, k, v, p->rope_cs, p->B, p->T, p->C, p->Hq, p->Hkv, p->D, (int)M, (int)N,
+                   tm, tn, (int)(((long)tm * tn + 7) / 8)};
+    return ne::launch_proj(a, static_cast<hipStream_t>(stream)) == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;

@@ -67,6 +67,19 @@ constexpr int kDecodeStages = 3;
 constexpr int kDecodeMaxWaves = 4096;
 constexpr int decode_merge_batch(int D) { return D == 128 ? 4 : 8; }
 
+struct ProjArgs {
+    const void* x;          // [M = B*T, C] bf16 activations, row-major
+    const void* w;          // [N = (Hq + 2 Hkv) D, C] bf16 packed weights, row-major
+    void* q;                // [B, Hq, T, D] rotated queries
+    void* k;                // [B, Hkv, T, D] rotated keys
+    void* v;                // [B, Hkv, T, D] values
+    const float* rope_cs;   // [rows][D/2][2] or nullptr (no rotation)
+    int B, T, C, Hq, Hkv, D;
+    int M, N;               // token rows and output features
+    int tiles_m, tiles_n;   // output tiles along tokens and features
+    int per_xcd;            // tiles per XCD (the grid is 8 * per_xcd workgroups)
+};
+
 struct RopeArgs {
     const void* x;
     void* y;
@@ -78,6 +91,9 @@ struct RopeArgs {
 };
 
 template <typename T, int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// tokens per output tile of the projection (multiple of 64) and the launch
+int proj_tile_tokens();
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

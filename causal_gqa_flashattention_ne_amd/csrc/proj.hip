@@ -1,0 +1,202 @@
+// proj.hip -- the query/key/value projection of an attention block on gfx950, with RoPE in the
+// epilogue and the outputs written straight into the attention layout [B, H, T, D].
+//
+// The model's linear maps carry no bias (agentlenshq NanoEuler page, "핵심 아키텍처 및 설계"); RoPE
+// rotates the queries and keys ("기술 사양").  Output feature f of token m is x[m] . w[f], the
+// features packed as [query heads | key heads | value heads], head-major, d fastest.
+//
+// GEMM in "TN" form: x [M, C] and w [N, C] both run along C, so every MFMA operand fragment is a
+// row read of an LDS tile (8 consecutive k per lane, no transposes).  The product is formed
+// feature-major, Y^T = W X^T: a lane of a 32 x 32 x 16 MFMA result holds one token and, per group
+// of four registers, four consecutive features, so each RoPE pair sits in one lane.  A workgroup
+// (4 waves, 2 x 2) owns 128 features x TOK tokens; k advances 64 per step through three LDS
+// stages filled by buffer loads straight into LDS (tiles.hpp), two steps ahead.  Results go through
+// padded LDS rows to 16-byte stores, each a run of 8 features of one (head, token) row.
+//
+// Placement: workgroup i runs on XCD i % 8.  Each XCD takes a contiguous range of tiles in
+// token-major order (features fastest), so the feature tiles of one token tile run back to back
+// on one XCD and read their x rows from its L2; w (2 MB at the 116M model) stays in every L2.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace ne {
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kFeat = 128;                 // features per output tile
+constexpr int kWT = 2;                     // 32-token MFMA tiles per wave along tokens
+constexpr int kTok = 2 * 32 * kWT;         // tokens per output tile
+constexpr int kK = 64;                     // k per step
+constexpr int kStagesP = 3;
+constexpr int kCPR = kK / 8;               // 16-byte chunks per tile row
+
+struct alignas(16) ProjLds {
+    alignas(16) bf16 w[kStagesP][kFeat * kK];   // [feature][k], swizzled
+    alignas(16) bf16 x[kStagesP][kTok * kK];    // [token][k], swizzled
+};
+// epilogue staging: [token][feature] bf16 rows padded by 8 elements (conflict-free 8-byte writes)
+constexpr int kOutPitch = kFeat + 8;
+static_assert(kTok * kOutPitch * 2 <= (int)sizeof(ProjLds), "output staging must fit in the stage buffers");
+
+// Copies of ROWS x 64 bf16 tiles of a row-major matrix with a row pitch of `pitch` bytes into
+// swizzled LDS tiles, by the 4 waves of a workgroup (the tile copy of tiles.hpp with a run-time
+// row pitch).  The per-lane offsets within a tile are loop-invariant; rows past the end of the
+// buffer read as zeros.
+template <int ROWS>
+struct PitchCopy {
+    static constexpr int NU = ROWS * kCPR / (64 * kBlockWaves);
+    static_assert(NU >= 1 && (ROWS * kCPR) % (64 * kBlockWaves) == 0, "tile chunks must cover the waves");
+    unsigned voff[NU];
+    __device__ inline void init(int w, int lane, unsigned pitch) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = (u * kBlockWaves + w) * 64 + lane;
+            const int r = idx / kCPR, slot = idx % kCPR;
+            voff[u] = (unsigned)r * pitch + (unsigned)((slot ^ Swz<kK>::f(r)) << 4);
+        }
+    }
+    __device__ inline void copy(i32x4 rsrc, unsigned origin, unsigned lds, int w) const {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) copy16_to_lds(rsrc, voff[u], origin, lds + (unsigned)(u * kBlockWaves + w) * 1024u);
+    }
+};
+
+__global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
+    using M = Mfma<bf16>;
+    using CW = PitchCopy<kFeat>;
+    using CX = PitchCopy<kTok>;
+    constexpr int kCopies = CW::NU + CX::NU;       // copies per wave per step
+    __shared__ ProjLds S;
+
+    // ---- tile of this workgroup ----
+    const int xcd = (int)blockIdx.x % kXcds, local = (int)blockIdx.x / kXcds;
+    const int tile = xcd * a.per_xcd + local;
+    if (local >= a.per_xcd || tile >= a.tiles_m * a.tiles_n) return;
+    const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+    const int m0 = tm * kTok, n0 = tn * kFeat;
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int wf = w >> 1, wt = w & 1;              // wave: features wf*64.., tokens wt*(32 kWT)..
+
+    const unsigned pitch = (unsigned)a.C * 2u;
+    const i32x4 rw = buffer_rsrc(a.w, (unsigned)a.N * pitch);
+    const i32x4 rx = buffer_rsrc(a.x, (unsigned)a.M * pitch);
+    const unsigned lw = lds_addr(&S.w[0][0]), lx = lds_addr(&S.x[0][0]);
+    CW cw;
+    CX cx;
+    cw.init(w, lane, pitch);
+    cx.init(w, lane, pitch);
+    const int nk = a.C / kK;
+    auto issue = [&](int t) {
+        const unsigned st = (unsigned)(t % kStagesP);
+        cw.copy(rw, (unsigned)n0 * pitch + (unsigned)(t * kK * 2), lw + st * (unsigned)(kFeat * kK * 2), w);
+        cx.copy(rx, (unsigned)m0 * pitch + (unsigned)(t * kK * 2), lx + st * (unsigned)(kTok * kK * 2), w);
+    };
+    issue(0);
+    if (nk > 1) issue(1);
+
+    int ra[2][4], rb[kWT][4];                       // fragment offsets: [block][k chunk of 16]
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) ra[fb][kc] = Swz<kK>::at(wf * 64 + fb * 32 + col, 16 * kc + 8 * half);
+#pragma unroll
+        for (int tb = 0; tb < kWT; ++tb) rb[tb][kc] = Swz<kK>::at(wt * 32 * kWT + tb * 32 + col, 16 * kc + 8 * half);
+    }
+    f32x16 acc[2][kWT];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < kWT; ++tb) acc[fb][tb] = f32x16{};
+
+    for (int t = 0; t < nk; ++t) {
+        if (t + 1 < nk) wait_vmcnt<kCopies>();
+        else wait_vmcnt<0>();
+        step_barrier();                             // every wave's copies of tile t have landed
+        if (t + 2 < nk) issue(t + 2);               // its stage was last read in step t - 1
+        const bf16* Ws = S.w[t % kStagesP];
+        const bf16* Xs = S.x[t % kStagesP];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            bf16x8 af[2], bfr[kWT];
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(Ws + ra[fb][kc]);
+#pragma unroll
+            for (int tb = 0; tb < kWT; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(Xs + rb[tb][kc]);
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                for (int tb = 0; tb < kWT; ++tb) acc[fb][tb] = M::mma(af[fb], bfr[tb], acc[fb][tb]);
+        }
+    }
+
+    // ---- epilogue: RoPE on query and key features, bf16, staged through LDS ----
+    const int nq = a.Hq * a.D, nqk = (a.Hq + a.Hkv) * a.D;
+    __syncthreads();                                // every wave is done with the stage buffers
+    bf16* out = reinterpret_cast<bf16*>(&S);
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+        const int nb = n0 + wf * 64 + fb * 32;      // first feature of this 32-feature block
+        const bool rot = a.rope_cs && nb < nqk;     // query or key features (a block never straddles)
+#pragma unroll
+        for (int tb = 0; tb < kWT; ++tb) {
+            const int tok = wt * 32 * kWT + tb * 32 + col;   // row within the tile
+            const int m = m0 + tok;
+            const int pos = (m < a.M ? m : 0) % a.T;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                float y[4] = {acc[fb][tb][4 * rq], acc[fb][tb][4 * rq + 1], acc[fb][tb][4 * rq + 2],
+                              acc[fb][tb][4 * rq + 3]};
+                const int fl = wf * 64 + fb * 32 + acc_row(4 * rq, half);   // feature within the tile
+                if (rot) {
+                    const int d = (n0 + fl) % a.D;
+                    const f32x4 c = *reinterpret_cast<const f32x4*>(a.rope_cs + (size_t)pos * a.D + d);
+                    const float y0 = y[0], y1 = y[1], y2 = y[2], y3 = y[3];
+                    y[0] = y0 * c[0] - y1 * c[1];
+                    y[1] = y0 * c[1] + y1 * c[0];
+                    y[2] = y2 * c[2] - y3 * c[3];
+                    y[3] = y2 * c[3] + y3 * c[2];
+                }
+                *reinterpret_cast<bf16x4*>(out + tok * kOutPitch + fl) = cvt4(y);
+            }
+        }
+    }
+    __syncthreads();
+    // 16-byte runs: 8 features of one token, inside one head (D is a multiple of 8)
+    constexpr int kRuns = kTok * kFeat / 8;
+#pragma unroll
+    for (int i = threadIdx.x; i < kRuns; i += kBlockThreads) {
+        const int tok = i / (kFeat / 8), f8 = (i % (kFeat / 8)) * 8;
+        const int m = m0 + tok, n = n0 + f8;
+        if (m >= a.M || n >= a.N) continue;
+        const bf16x8 val = *reinterpret_cast<const bf16x8*>(out + tok * kOutPitch + f8);
+        const int b = m / a.T, tpos = m % a.T;
+        bf16* dst;
+        int head, d;
+        if (n < nq) {
+            head = n / a.D, d = n % a.D;
+            dst = reinterpret_cast<bf16*>(a.q) + (((size_t)b * a.Hq + head) * a.T + tpos) * a.D + d;
+        } else if (n < nqk) {
+            head = (n - nq) / a.D, d = (n - nq) % a.D;
+            dst = reinterpret_cast<bf16*>(a.k) + (((size_t)b * a.Hkv + head) * a.T + tpos) * a.D + d;
+        } else {
+            head = (n - nqk) / a.D, d = (n - nqk) % a.D;
+            dst = reinterpret_cast<bf16*>(a.v) + (((size_t)b * a.Hkv + head) * a.T + tpos) * a.D + d;
+        }
+        *reinterpret_cast<bf16x8*>(dst) = val;
+    }
+}
+
+}  // namespace
+
+int proj_tile_tokens() { return kTok; }
+
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(proj_kernel, dim3((unsigned)(kXcds * a.per_xcd)), dim3(kBlockThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ne

@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"fwd_bf16_kernel": "fwd", "bwd_pre_bf16_kernel": "bwd_pre", "bwd_bf16_kernel": "bwd_main",
            "fwd_kernel": "fwd", "bwd_pre_kernel": "bwd_pre", "bwd_main_kernel": "bwd_main",
            "rope_apply_kernel": "rope_keys", "decode_split_kernel": "decode_split",
-           "decode_merge_kernel": "decode_merge", "decode16_kernel": "decode16"}
+           "decode_merge_kernel": "decode_merge", "decode16_kernel": "decode16",
+           "proj_kernel": "qkv_proj"}
 CAL_BYTES = 256 << 20
 
 

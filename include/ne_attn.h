@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 4
+#define NE_ABI_VERSION 5
 
 enum {
     NE_OK = 0,
@@ -188,6 +188,30 @@ size_t ne_attn_decode_workspace_bytes(const ne_decode_params* p);
 int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* kv_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * The query, key and value projections of an attention block, with RoPE on the queries and keys,
+ * written straight into the attention layout (the bias-free linear maps before the attention:
+ * agentlenshq NanoEuler page, "핵심 아키텍처 및 설계"; RoPE on queries and keys: "기술 사양").
+ *   x  [B, T, C] bf16, row-major: the normalised activations of B sequences of T tokens.
+ *   w  [(Hq + 2 Hkv) D, C] bf16, row-major: packed weights, output feature f = x . w[f]; the
+ *      features are [query heads | key heads | value heads], head-major, d fastest in each head.
+ *   q  [B, Hq, T, D] bf16: R_t (x W_q^T) for the token at position t (0-based within its sequence);
+ *   k  [B, Hkv, T, D] bf16: R_t (x W_k^T);  v [B, Hkv, T, D] bf16: x W_v^T.  No RoPE when
+ *      rope_cs is NULL.  Outputs are fully overwritten; x and w are not written.
+ * bf16 only; D in {32, 64, 128}; C a multiple of 64; B*T*C and (Hq + 2 Hkv)*D*C below 2^31.
+ * fp32 accumulation, one rounding to bf16 per output.  One launch on stream; no workspace.
+ */
+typedef struct ne_qkv_params {
+    int32_t B, T, C;           /* sequences, tokens per sequence, model width */
+    int32_t Hq, Hkv, D;        /* query heads, kv heads, head_dim */
+    int32_t dtype;             /* NE_DTYPE_BF16 */
+    const float* rope_cs;      /* device RoPE table with >= T rows (ne_rope_table), or NULL */
+    int32_t rope_rows;
+} ne_qkv_params;
+
+int ne_qkv_proj(const ne_qkv_params* p, const void* x, const void* w, void* q, void* k, void* v,
+                void* stream);
 
 #ifdef __cplusplus
 }

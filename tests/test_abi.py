@@ -200,3 +200,43 @@ def test_decode_dtype_pointers_workspace():
     assert dec(p, ptrs=ptrs) == -4
     p.rope_cs, p.rope_rows = ALIGNED, 127   # table shorter than the cache
     assert dec(p) == -2
+
+
+def qparams(**kw):
+    base = dict(B=2, T=16, C=128, Hq=4, Hkv=2, D=64)
+    base.update(kw)
+    return ne.make_qkv_params(**base)
+
+
+def qkv(p, ptrs=None):
+    vp = ctypes.c_void_p
+    ptrs = ptrs or [ALIGNED] * 5
+    return ne.lib().ne_qkv_proj(ctypes.byref(p), *[vp(x) for x in ptrs], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2),
+    (dict(T=-1), -2),
+    (dict(Hkv=0), -2),
+    (dict(C=96), -3),                        # C must be a multiple of 64
+    (dict(D=48), -3),
+    (dict(B=1 << 16, T=1 << 10, C=1 << 6), -2),
+])
+def test_qkv_rejects_bad_shapes(kw, code):
+    assert qkv(qparams(**kw)) == code
+
+
+def test_qkv_dtype_pointers_table():
+    p = qparams()
+    p.dtype = ne.NE_DTYPE_F32
+    assert qkv(p) == -3                      # bf16 only
+    p = qparams()
+    ptrs = [ALIGNED] * 5
+    ptrs[1] = 0                              # w
+    assert qkv(p, ptrs=ptrs) == -1
+    ptrs[1] = MISALIGNED
+    assert qkv(p, ptrs=ptrs) == -4
+    p.rope_cs, p.rope_rows = ALIGNED, 15     # T = 16
+    assert qkv(p) == -2
+    p.rope_cs, p.rope_rows = MISALIGNED, 16
+    assert qkv(p) == -4
