@@ -9,9 +9,11 @@
 // row read of an LDS tile (8 consecutive k per lane, no transposes).  The product is formed
 // feature-major, Y^T = W X^T: a lane of a 32 x 32 x 16 MFMA result holds one token and, per group
 // of four registers, four consecutive features, so each RoPE pair sits in one lane.  A workgroup
-// (4 waves, 2 x 2) owns 128 features x TOK tokens; k advances 64 per step through three LDS
-// stages filled by buffer loads straight into LDS (tiles.hpp), two steps ahead.  Results go through
-// padded LDS rows to 16-byte stores, each a run of 8 features of one (head, token) row.
+// (4 waves, 2 x 2) owns 128 features x 128 tokens; k advances 64 per step through two LDS stages
+// filled by buffer loads straight into LDS (tiles.hpp), one step ahead; at 64 KiB two workgroups
+// share a CU and overlap each other's waits (measured faster than three or four stages with one
+// workgroup per CU, and than 64- or 256-token tiles).  Results go through padded LDS rows to
+// 16-byte stores, each a run of 8 features of one (head, token) row.
 //
 // Placement: workgroup i runs on XCD i % 8.  Each XCD takes a contiguous range of tiles in
 // token-major order (features fastest), so the feature tiles of one token tile run back to back
@@ -29,7 +31,7 @@ constexpr int kFeat = 128;                 // features per output tile
 constexpr int kWT = 2;                     // 32-token MFMA tiles per wave along tokens
 constexpr int kTok = 2 * 32 * kWT;         // tokens per output tile
 constexpr int kK = 64;                     // k per step
-constexpr int kStagesP = 3;
+constexpr int kStagesP = 2;               // 64 KiB of LDS: two workgroups per CU
 constexpr int kCPR = kK / 8;               // 16-byte chunks per tile row
 
 struct alignas(16) ProjLds {
@@ -63,6 +65,16 @@ struct PitchCopy {
     }
 };
 
+// q = m / d and r = m - q d for 0 <= m < 2^31, d >= 1: a double-precision estimate (exact to
+// within one) corrected once each way
+__device__ inline void divmod(int m, int d, double inv_d, int& q, int& r) {
+    q = (int)((double)m * inv_d);
+    r = m - q * d;
+    if (r < 0) --q, r += d;
+    else if (r >= d) ++q, r -= d;
+}
+
+template <bool ROPE>
 __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
     using M = Mfma<bf16>;
     using CW = PitchCopy<kFeat>;
@@ -81,6 +93,10 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
     const int col = lane & 31, half = lane >> 5;
     const int wf = w >> 1, wt = w & 1;              // wave: features wf*64.., tokens wt*(32 kWT)..
 
+    // D is a power of two (32, 64 or 128): head and d by shift and mask
+    const int lgD = __builtin_ctz(a.D);
+    const int nq = a.Hq << lgD, nqk = (a.Hq + a.Hkv) << lgD;
+    const double invT = 1.0 / (double)a.T;
     const unsigned pitch = (unsigned)a.C * 2u;
     const i32x4 rw = buffer_rsrc(a.w, (unsigned)a.N * pitch);
     const i32x4 rx = buffer_rsrc(a.x, (unsigned)a.M * pitch);
@@ -95,8 +111,38 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
         cw.copy(rw, (unsigned)n0 * pitch + (unsigned)(t * kK * 2), lw + st * (unsigned)(kFeat * kK * 2), w);
         cx.copy(rx, (unsigned)m0 * pitch + (unsigned)(t * kK * 2), lx + st * (unsigned)(kTok * kK * 2), w);
     };
-    issue(0);
-    if (nk > 1) issue(1);
+#pragma unroll
+    for (int i = 0; i < kStagesP - 1; ++i)
+        if (i < nk) issue(i);
+    // every table entry this lane needs, loaded right after the first tiles are requested and
+    // pinned here: the compiler's wait for them (vmcnt 0) then also covers those tiles, whose
+    // latency it overlaps, and no copy is in flight behind it
+    f32x4 cs[2][kWT][4];
+    bool rot[2];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) rot[fb] = ROPE && n0 + wf * 64 + fb * 32 < nqk;   // whole 32-blocks
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int tb = 0; tb < kWT; ++tb) {
+            const int m = m0 + wt * 32 * kWT + tb * 32 + col;
+            int bq, pos;
+            divmod(m < a.M ? m : 0, a.T, invT, bq, pos);
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d = (n0 + wf * 64 + fb * 32 + acc_row(4 * rq, half)) & (a.D - 1);
+                    cs[fb][tb][rq] = *reinterpret_cast<const f32x4*>(a.rope_cs + (size_t)pos * a.D + d);
+                }
+        }
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int tb = 0; tb < kWT; ++tb)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) asm volatile("" : "+v"(cs[fb][tb][rq]));
+    }
+
 
     int ra[2][4], rb[kWT][4];                       // fragment offsets: [block][k chunk of 16]
 #pragma unroll
@@ -113,10 +159,16 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
         for (int tb = 0; tb < kWT; ++tb) acc[fb][tb] = f32x16{};
 
     for (int t = 0; t < nk; ++t) {
-        if (t + 1 < nk) wait_vmcnt<kCopies>();
-        else wait_vmcnt<0>();
+        // this wave's copies of tile t have landed when at most the later tiles' are in flight
+        static_assert(kStagesP == 2 || kStagesP == 3, "wait counts below are for two or three stages");
+        if constexpr (kStagesP == 3) {
+            if (t + 1 < nk) wait_vmcnt<(kStagesP - 2) * kCopies>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         step_barrier();                             // every wave's copies of tile t have landed
-        if (t + 2 < nk) issue(t + 2);               // its stage was last read in step t - 1
+        if (t + kStagesP - 1 < nk) issue(t + kStagesP - 1);   // its stage was last read in step t - 1
         const bf16* Ws = S.w[t % kStagesP];
         const bf16* Xs = S.x[t % kStagesP];
 #pragma unroll
@@ -134,31 +186,24 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
     }
 
     // ---- epilogue: RoPE on query and key features, bf16, staged through LDS ----
-    const int nq = a.Hq * a.D, nqk = (a.Hq + a.Hkv) * a.D;
     __syncthreads();                                // every wave is done with the stage buffers
     bf16* out = reinterpret_cast<bf16*>(&S);
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb) {
-        const int nb = n0 + wf * 64 + fb * 32;      // first feature of this 32-feature block
-        const bool rot = a.rope_cs && nb < nqk;     // query or key features (a block never straddles)
 #pragma unroll
         for (int tb = 0; tb < kWT; ++tb) {
             const int tok = wt * 32 * kWT + tb * 32 + col;   // row within the tile
-            const int m = m0 + tok;
-            const int pos = (m < a.M ? m : 0) % a.T;
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 float y[4] = {acc[fb][tb][4 * rq], acc[fb][tb][4 * rq + 1], acc[fb][tb][4 * rq + 2],
                               acc[fb][tb][4 * rq + 3]};
                 const int fl = wf * 64 + fb * 32 + acc_row(4 * rq, half);   // feature within the tile
-                if (rot) {
-                    const int d = (n0 + fl) % a.D;
-                    const f32x4 c = *reinterpret_cast<const f32x4*>(a.rope_cs + (size_t)pos * a.D + d);
+                if constexpr (ROPE) {
+                    const f32x4 c = cs[fb][tb][rq];
                     const float y0 = y[0], y1 = y[1], y2 = y[2], y3 = y[3];
-                    y[0] = y0 * c[0] - y1 * c[1];
-                    y[1] = y0 * c[1] + y1 * c[0];
-                    y[2] = y2 * c[2] - y3 * c[3];
-                    y[3] = y2 * c[3] + y3 * c[2];
+                    const float r0 = y0 * c[0] - y1 * c[1], r1 = y0 * c[1] + y1 * c[0];
+                    const float r2 = y2 * c[2] - y3 * c[3], r3 = y2 * c[3] + y3 * c[2];
+                    if (rot[fb]) y[0] = r0, y[1] = r1, y[2] = r2, y[3] = r3;
                 }
                 *reinterpret_cast<bf16x4*>(out + tok * kOutPitch + fl) = cvt4(y);
             }
@@ -173,18 +218,17 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
         const int m = m0 + tok, n = n0 + f8;
         if (m >= a.M || n >= a.N) continue;
         const bf16x8 val = *reinterpret_cast<const bf16x8*>(out + tok * kOutPitch + f8);
-        const int b = m / a.T, tpos = m % a.T;
+        int b, tpos;
+        divmod(m, a.T, invT, b, tpos);
         bf16* dst;
-        int head, d;
         if (n < nq) {
-            head = n / a.D, d = n % a.D;
-            dst = reinterpret_cast<bf16*>(a.q) + (((size_t)b * a.Hq + head) * a.T + tpos) * a.D + d;
+            dst = reinterpret_cast<bf16*>(a.q) + ((((size_t)b * a.Hq + (n >> lgD)) * a.T + tpos) << lgD) + (n & (a.D - 1));
         } else if (n < nqk) {
-            head = (n - nq) / a.D, d = (n - nq) % a.D;
-            dst = reinterpret_cast<bf16*>(a.k) + (((size_t)b * a.Hkv + head) * a.T + tpos) * a.D + d;
+            const int nn = n - nq;
+            dst = reinterpret_cast<bf16*>(a.k) + ((((size_t)b * a.Hkv + (nn >> lgD)) * a.T + tpos) << lgD) + (nn & (a.D - 1));
         } else {
-            head = (n - nqk) / a.D, d = (n - nqk) % a.D;
-            dst = reinterpret_cast<bf16*>(a.v) + (((size_t)b * a.Hkv + head) * a.T + tpos) * a.D + d;
+            const int nn = n - nqk;
+            dst = reinterpret_cast<bf16*>(a.v) + ((((size_t)b * a.Hkv + (nn >> lgD)) * a.T + tpos) << lgD) + (nn & (a.D - 1));
         }
         *reinterpret_cast<bf16x8*>(dst) = val;
     }
@@ -195,7 +239,8 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
 int proj_tile_tokens() { return kTok; }
 
 hipError_t launch_proj(const ProjArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(proj_kernel, dim3((unsigned)(kXcds * a.per_xcd)), dim3(kBlockThreads), 0, stream, a);
+    if (a.rope_cs) hipLaunchKernelGGL(proj_kernel<true>, dim3((unsigned)(kXcds * a.per_xcd)), dim3(kBlockThreads), 0, stream, a);
+    else hipLaunchKernelGGL(proj_kernel<false>, dim3((unsigned)(kXcds * a.per_xcd)), dim3(kBlockThreads), 0, stream, a);
     return hipGetLastError();
 }
 
