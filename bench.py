@@ -71,9 +71,9 @@ def measured_traffic(workload, kernel):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_sha256") != profsum.source_hash() or kernel not in t.get("kernels", {}):
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or k.get("source_sha256") != profsum.source_hash(kernel):
         return None
-    k = t["kernels"][kernel]
     return k["read_bytes"] + k["write_bytes"]
 
 

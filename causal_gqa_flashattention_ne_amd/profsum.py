@@ -6,7 +6,7 @@
         per-kernel HBM bytes per dispatch from two counter runs (--pmc FETCH_SIZE, then
         --pmc WRITE_SIZE) of `bench.py --copy-calibration`, each scaled by what the same counter
         reads for the calibration copy (256 MiB read + 256 MiB written per launch), tagged with a
-        hash of the kernel sources so that the benchmark stops quoting it once a kernel changes.
+        hash of each kernel's sources so that the benchmark stops quoting it once that kernel changes.
 """
 import collections
 import csv
@@ -26,9 +26,25 @@ KERNELS = {"fwd_bf16_kernel": "fwd", "bwd_pre_bf16_kernel": "bwd_pre", "bwd_bf16
 CAL_BYTES = 256 << 20
 
 
-def source_hash() -> str:
+# the sources each kernel is built from (shared headers included); a stored traffic figure stays
+# valid while these hash the same
+_HEADERS = ("common.hpp", "tiles.hpp", "kernels.hpp")
+KERNEL_SOURCES = {
+    "fwd": ("fwd_bf16.hip", "fwd.hip"), "bwd_pre": ("bwd_bf16.hip", "bwd.hip"), "bwd_main": ("bwd_bf16.hip", "bwd.hip"),
+    "rope_keys": ("rope.hip",), "decode16": ("decode.hip",), "decode_split": ("decode.hip",),
+    "decode_merge": ("decode.hip",), "qkv_proj": ("proj.hip",),
+}
+
+
+def source_hash(kernel=None) -> str:
+    """sha256 over the sources of `kernel` (a short name of KERNELS) and the shared headers, or over
+    every source file when kernel is None."""
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(HERE, "csrc", "*")))
+    else:
+        files = [os.path.join(HERE, "csrc", f) for f in sorted(KERNEL_SOURCES[kernel] + _HEADERS)]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+    for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -49,12 +65,13 @@ def traffic(fetch_dir, write_dir, out):
         raise SystemExit("no calibration copy kernel in %s" % fetch_dir)
     rf = CAL_BYTES / fetch[cal[0]]
     wf = CAL_BYTES / write[cal[0]]
-    res = {"source_sha256": source_hash(), "read_scale": rf, "write_scale": wf, "kernels": {}}
+    res = {"read_scale": rf, "write_scale": wf, "kernels": {}}
     for name in fetch:
         for key, short in KERNELS.items():
             if key + "<" in name or name.endswith(key) or ("::" + key + "(") in name:
                 res["kernels"][short] = {"name": name, "read_bytes": fetch[name] * rf,
-                                         "write_bytes": write.get(name, 0.0) * wf}
+                                         "write_bytes": write.get(name, 0.0) * wf,
+                                         "source_sha256": source_hash(short)}
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
