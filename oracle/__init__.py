@@ -172,3 +172,51 @@ def qkv_proj(x, w, Hq, Hkv, theta=10000.0):
     if theta > 0:
         q, k = rope(q, theta), rope(k, theta)
     return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def rmsnorm(x, g, eps=1e-5):
+    """x / sqrt(mean(x^2) + eps) * g over the last axis (bias-free pre-normalisation: agentlenshq
+    NanoEuler page, "기술 사양")."""
+    x = _d(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _d(g)
+
+
+def block(x, g, wqkv, wo, dy, Hq, Hkv, theta=10000.0, eps=1e-5):
+    """One pre-norm attention block and its gradients, in double:
+
+        xn = rmsnorm(x, g);  q, k, v = qkv_proj(xn, wqkv)  (RoPE on q and k);
+        o = causal GQA attention(q, k, v);  y = x + concat_heads(o) wo^T
+
+    (the block order of the agentlenshq NanoEuler page, "기술 사양": RMSNorm pre-normalisation,
+    RoPE on queries and keys, GQA; bias-free linear maps).  x [B, T, C], g [C], wqkv
+    [(Hq + 2 Hkv) D, C], wo [C, Hq D], dy [B, T, C] the gradient of the loss with respect to y.
+    Returns (y, dx, dg, dwqkv, dwo).  The backward is the chain rule written out step by step, the
+    attention part through ``attention``'s own backward; the tests pin it to central finite
+    differences.
+    """
+    x, g, wqkv, wo, dy = _d(x), _d(g), _d(wqkv), _d(wo), _d(dy)
+    B, T, C = x.shape
+    N = wqkv.shape[0]
+    D = N // (Hq + 2 * Hkv)
+    # forward
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)     # [B, T, 1]
+    u = x / r
+    xn = u * g
+    q, k, v = qkv_proj(xn, wqkv, Hq, Hkv, theta=theta)              # rotated q, k
+    o, _ = attention(q, k, v, theta=0.0)
+    oc = o.transpose(0, 2, 1, 3).reshape(B, T, Hq * D)              # heads concatenated
+    y = x + oc @ wo.T
+    # backward
+    dwo = np.einsum("btc,btj->cj", dy, oc)
+    doc = dy @ wo                                                   # [B, T, Hq D]
+    do = doc.reshape(B, T, Hq, D).transpose(0, 2, 1, 3)
+    _, _, dq, dk, dv = attention(q, k, v, do, theta=0.0)            # w.r.t. the rotated q, k
+    if theta > 0:
+        dq, dk = rope(dq, theta, inverse=True), rope(dk, theta, inverse=True)
+    dyp = np.concatenate([dq, dk, dv], axis=1).transpose(0, 2, 1, 3).reshape(B, T, N)
+    dwqkv = np.einsum("btn,btc->nc", dyp, xn)
+    dxn = dyp @ wqkv
+    dg = np.einsum("btc,btc->c", dxn, u)
+    du = dxn * g
+    dx = dy + du / r - x * np.sum(du * x, axis=-1, keepdims=True) / (C * r ** 3)
+    return y, dx, dg, dwqkv, dwo
