@@ -15,6 +15,11 @@ With --qkv 1, the step is one call of the query/key/value projection (ne_qkv_pro
 RoPE on queries and keys, written into the attention layout) on the 116M model's shapes, and
 value = its TFLOP/s (2 * B*T * C * (Hq + 2 Hkv) D per call).
 
+With --block 1, the step is one forward + backward of a pre-norm attention block of the 116M
+model (block.py: RMSNorm, the projection, attention, output projection, residual; the library's
+kernels for the projection, attention and RoPE, torch float32 for the rest), and value = its
+algorithmic TFLOP/s.
+
 With --decode D, the step is instead one decode call (ne_attn_decode: n new tokens per sequence
 against a rotated bf16 KV cache, split over the key range and merged) on decode workload D, and
 value = algorithmic HBM GB/s of that call (cache rows read once, queries read, outputs written).
@@ -42,6 +47,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
     ap.add_argument("--decode", type=int, default=0, help="decode workload id 1..2 instead of the training step")
     ap.add_argument("--qkv", type=int, default=0, help="projection workload id (1) instead of the training step")
+    ap.add_argument("--block", type=int, default=0, help="1: attention block forward + backward instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,6 +106,8 @@ def main():
         return bench_decode(args, dev)
     if args.qkv:
         return bench_qkv(args, dev)
+    if args.block:
+        return bench_block(args, dev)
     w = gen.WORKLOADS[args.workload]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4
@@ -343,6 +351,82 @@ def bench_qkv(args, dev):
     }
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(dev)
+    print(json.dumps(out))
+
+
+def bench_block(args, dev):
+    import torch
+
+    import causal_gqa_flashattention_ne_amd as ne
+    import gen
+    from causal_gqa_flashattention_ne_amd.block import block_forward_backward
+
+    w = gen.QKV_WORKLOADS[1]                       # the 116M model's block: B 16, T 512, C 768
+    B, T, C, Hq, Hkv, D = w.B, w.T, w.C, w.Hq, w.Hkv, w.D
+    x, wqkv = gen.qkv_case(w.seed, B, T, C, Hq, Hkv, D)
+    rng = np.random.default_rng(w.seed)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16).contiguous()
+    xd, wd = t(x), t(wqkv)
+    g = t(1.0 + 0.1 * rng.standard_normal(C))
+    wo = t(rng.standard_normal((C, Hq * D)) / np.sqrt(Hq * D))
+    dy = t(rng.standard_normal((B, T, C)))
+
+    def step():
+        return block_forward_backward(xd, g, wd, wo, dy, Hq, Hkv, rope_theta=w.theta)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    M, N = B * T, (Hq + 2 * Hkv) * D
+    pairs = B * Hq * T * (T + 1) // 2
+    proj = 2 * M * C * N + 2 * M * Hq * D * C            # projection and output projection, forward
+    flop = 3 * proj + 14 * D * pairs                     # backward products twice the forward's
+    out = {
+        "metric": "pre-norm attention block forward+backward, algorithmic TFLOP/s",
+        "value": flop / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normals)",
+        "config": {"workload": "gpt116m-block-bf16", "B": B, "T": T, "C": C, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "rope_theta": w.theta, "parallelism": "none (1 GPU)"},
+        "algorithmic_flop": flop,
+        "roofline": None,            # a composition: each library kernel has its own bench mode
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        xs, ws, gs, wos, dys = x[:1], wqkv, g.float().cpu().numpy(), wo.float().cpu().numpy(), dy[:1].float().cpu().numpy()
+        flop1 = flop / B                                 # one sequence
+        with threadpool_limits(limits=threads):
+            t_s = time.perf_counter()
+            passes = 0
+            while True:                                  # one sequence's block, for >= 2 s
+                oracle.block(xs, gs, ws, wos, dys, Hq, Hkv, theta=w.theta)
+                passes += 1
+                if time.perf_counter() - t_s >= 2.0:
+                    break
+            dt = time.perf_counter() - t_s
+        out["cpu_baseline"] = {"value": flop1 * passes / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                               "kind": "oracle", "sample": "1 of %d sequences x %d passes, block forward + "
+                               "backward in double, %.2f s wall" % (B, passes, dt)}
     print(json.dumps(out))
 
 
