@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: causal GQA attention forward + backward on one MI355X, through the C ABI.
 
-A step is one pass of the whole hot path over one batch of synthetic input: RoPE-fused forward
-(O and L) then the backward (delta preprocess and the main kernel: dQ, dK, dV), for every layer
-of the workload.  Inputs are resident in HBM before the timed region; outputs and workspace are
+A step is one pass of the whole hot path over one batch of synthetic input, through the library's
+training pair: the RoPE-fused forward (O and L; it also leaves the rotated queries and keys in the
+shared workspace) then the backward (the delta preprocess and the main kernel: dQ, dK, dV), for
+every layer of the workload.  Inputs are resident in HBM before the timed region; outputs and workspace are
 preallocated; nothing is allocated or copied inside it.
 
 Prints ONE JSON line.  value = whole-job algorithmic TFLOP/s with the causal pairs counted exactly:
@@ -123,8 +124,7 @@ def main():
         layers.append(t)
     cs = ne.rope_table(w.T, w.D, w.theta, dev)
     p = ne.make_params(w.B, w.Hq, w.Hkv, w.T, w.D, ne._dtype_code(layers[0][0]), None, cs)
-    ws = torch.empty(ne.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    fws = torch.empty(max(1, ne.fwd_workspace_bytes(p)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ne.bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)   # shared by the pair
     outs = []
     for (q, k, v, do) in layers:
         outs.append((torch.empty_like(q), torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev),
@@ -136,10 +136,10 @@ def main():
         for li, ((q, k, v, do), (o, lse, dq, dk, dv)) in enumerate(zip(layers, outs)):
             if ev is not None:
                 ev[0][li].record(stream)
-            ne.attn_fwd_into(p, q, k, v, o, lse, fws, st)
+            ne.attn_fwd_train_into(p, q, k, v, o, lse, ws, st)
             if ev is not None:
                 ev[1][li].record(stream)
-            ne.attn_bwd_preprocess_into(p, q, k, o, lse, do, ws, st)
+            ne.attn_bwd_train_preprocess_into(p, q, k, o, lse, do, ws, st)
             if ev is not None:
                 ev[2][li].record(stream)
             ne.attn_bwd_main_into(p, q, k, v, lse, do, dq, dk, dv, ws, st)

@@ -27,11 +27,12 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
            "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main",
-           "ne_attn_decode_workspace_bytes", "ne_attn_decode", "ne_qkv_proj")
+           "ne_attn_decode_workspace_bytes", "ne_attn_decode", "ne_qkv_proj", "ne_attn_fwd_train",
+           "ne_attn_bwd_train", "ne_attn_bwd_train_preprocess")
 
 
 class AttnParams(ctypes.Structure):
@@ -95,8 +96,12 @@ def lib():
         L.ne_attn_decode_workspace_bytes.restype = sz
         L.ne_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 7 + [sz, vp]
         L.ne_qkv_proj.argtypes = [ctypes.POINTER(QkvParams)] + [vp] * 6
+        L.ne_attn_fwd_train.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ne_attn_bwd_train.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
+        L.ne_attn_bwd_train_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
-                  "ne_attn_bwd_main", "ne_attn_decode", "ne_qkv_proj"):
+                  "ne_attn_bwd_main", "ne_attn_decode", "ne_qkv_proj", "ne_attn_fwd_train", "ne_attn_bwd_train",
+                  "ne_attn_bwd_train_preprocess"):
             getattr(L, f).restype = ctypes.c_int
         if L.ne_abi_version() != ABI_VERSION:
             raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
@@ -356,3 +361,38 @@ def qkv_proj(x, w, Hq: int, Hkv: int, rope_theta: float = 10000.0):
     v = torch.empty_like(k)
     qkv_proj_into(p, x, w, q, k, v)
     return q, k, v
+
+
+def attn_fwd_train_into(p: AttnParams, q, k, v, o, lse, ws, stream=None):
+    """Training forward into preallocated o / lse, leaving the backward's rotated operands in ws
+    (uint8, >= bwd_workspace_bytes(p)); pass the same ws to attn_bwd_train_into."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_fwd_train", lib().ne_attn_fwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                         _ptr(ws), ws.numel() * ws.element_size(), st))
+
+
+def attn_bwd_train_preprocess_into(p: AttnParams, q, k, o, lse, do, ws, stream=None):
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_bwd_train_preprocess",
+           lib().ne_attn_bwd_train_preprocess(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(o), _ptr(lse), _ptr(do), _ptr(ws),
+                                              ws.numel() * ws.element_size(), st))
+
+
+def attn_bwd_train_into(p: AttnParams, q, k, v, o, lse, do, dq, dk, dv, ws, stream=None):
+    """Training backward (after attn_fwd_train_into with the same ws) into preallocated gradients."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_bwd_train", lib().ne_attn_bwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                         _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                                         ws.numel() * ws.element_size(), st))
+
+
+def attn_train(q, k, v, do, rope_theta: float = 10000.0, scale=None):
+    """Forward and backward through the training pair.  Returns (o, lse, dq, dk, dv)."""
+    p, _ = _params_for(q, k, rope_theta, scale)
+    ws = torch.empty(bwd_workspace_bytes(p), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_train_into(p, q, k, v, o, lse, ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd_train_into(p, q, k, v, o, lse, do, dq, dk, dv, ws)
+    return o, lse, dq, dk, dv

@@ -349,6 +349,64 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
     });
 }
 
+int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (p->dtype != NE_DTYPE_BF16) return ne_attn_fwd(p, q, k, v, o, lse, nullptr, 0, stream);
+    if (int rc = check_ptrs({q, k, v, o, lse, workspace})) return rc;
+    ne::BwdArgs b;
+    if (int rc = bwd_args(p, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, &b))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ne::FwdArgs a{q, b.krot, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p), b.qrot, b.qrot_lo};
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        using T = decltype(t);
+        constexpr int DD = decltype(d)::value;
+        if constexpr (std::is_same<T, ne::bf16>::value) {
+            // the keys as the backward reads them: rotated once here, or copied when there is no RoPE
+            hipError_t e;
+            if (p->rope_cs) {
+                ne::RopeArgs r{k, b.krot, p->rope_cs, p->B * p->Hkv * p->T, p->T, 0, 0};
+                e = ne::launch_rope<T, DD>(r, s);
+            } else {
+                e = hipMemcpyAsync(b.krot, k, (size_t)p->B * p->Hkv * p->T * DD * sizeof(T), hipMemcpyDeviceToDevice, s);
+            }
+            if (e != hipSuccess) return e;
+            return ne::launch_fwd_bf16<DD>(a, s);
+        } else {
+            return hipErrorInvalidValue;            // not reached: float32 returned above
+        }
+    });
+}
+
+int ne_attn_bwd_train_preprocess(const ne_attn_params* p, const void* q, const void* k, const void* o,
+                                 const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (p->dtype != NE_DTYPE_BF16) return ne_attn_bwd_preprocess(p, q, k, o, lse, dout, workspace, workspace_bytes, stream);
+    if (int rc = check_ptrs({q, k, o, lse, dout, workspace})) return rc;
+    ne::BwdArgs a;
+    if (int rc = bwd_args(p, q, k, nullptr, o, lse, dout, nullptr, nullptr, nullptr,
+                          workspace, workspace_bytes, &a)) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch(p->dtype, p->D, [&](auto t, auto d) {
+        using T = decltype(t);
+        constexpr int DD = decltype(d)::value;
+        if constexpr (std::is_same<T, ne::bf16>::value) return ne::launch_bwd_pre_bf16<DD>(a, s, false);
+        else return hipErrorInvalidValue;        // not reached: float32 returned above
+    });
+}
+
+int ne_attn_bwd_train(const ne_attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (int rc = check_attn(p)) return rc;
+    if (int rc = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return rc;
+    if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
+    if (int rc = ne_attn_bwd_train_preprocess(p, q, k, o, lse, dout, workspace, workspace_bytes, stream)) return rc;
+    return ne_attn_bwd_main(p, q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
 int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, const void* v,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream) {

@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_bf16_kernel(BwdArgs a) {
 // Per query row (padded per head to Tp rows): delta = sum_d dO O and l' = L log2(e) -
 // log2(scale) (rows past T: 0 and +inf) into the tile layout of ld_lsc; Q~ = R q as bf16 hi + lo;
 // then K~ = R k (bf16).
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
     constexpr int TPR = D / 8;
     const long qrows = (long)a.B * a.Hq * a.Tp;
@@ -500,16 +500,19 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
         float sum = 0.f;
         if (t < a.T) {
             const size_t off = ((size_t)bh * a.T + t) * D + part * 8;
-            float o[8], d[8], q[8];
+            float o[8], d[8];
             load16<bf16>(reinterpret_cast<const bf16*>(a.o) + off, o);
             load16<bf16>(reinterpret_cast<const bf16*>(a.dout) + off, d);
-            load16<bf16>(reinterpret_cast<const bf16*>(a.q) + off, q);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sum += o[e] * d[e];
-            if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, t, part * 8, false);
-            const bf16x8 hi = cvt8(q);
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) = remainder8(q, hi);
+            if constexpr (ROT) {
+                float q[8];
+                load16<bf16>(reinterpret_cast<const bf16*>(a.q) + off, q);
+                if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, t, part * 8, false);
+                const bf16x8 hi = cvt8(q);
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) = remainder8(q, hi);
+            }
         }
 #pragma unroll
         for (int o2 = 1; o2 < TPR; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
             ldt[ld_lsc(r)] = t < a.T ? a.lse[bh * a.T + t] * kLog2e - __log2f(a.scale) : INFINITY;
             ldt[ld_dlt(r)] = sum;
         }
-    } else if (row < qrows + krows) {
+    } else if (ROT && row < qrows + krows) {
         const long kr = row - qrows;
         const size_t off = (size_t)kr * D + part * 8;
         float k[8];
@@ -532,11 +535,12 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
 }  // namespace
 
 template <int D>
-hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream) {
-    const long rows = (long)a.B * a.Hq * a.Tp + (long)a.B * a.Hkv * a.T;
+hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream, bool rotate) {
+    const long rows = (long)a.B * a.Hq * a.Tp + (rotate ? (long)a.B * a.Hkv * a.T : 0L);
     const long threads = rows * (D / 8);
-    hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, a);
+    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    if (rotate) hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -548,9 +552,9 @@ hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template hipError_t launch_bwd_pre_bf16<128>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_pre_bf16<64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_pre_bf16<32>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_pre_bf16<128>(const BwdArgs&, hipStream_t, bool);
+template hipError_t launch_bwd_pre_bf16<64>(const BwdArgs&, hipStream_t, bool);
+template hipError_t launch_bwd_pre_bf16<32>(const BwdArgs&, hipStream_t, bool);
 template hipError_t launch_bwd_main_bf16<128>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main_bf16<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main_bf16<32>(const BwdArgs&, hipStream_t);

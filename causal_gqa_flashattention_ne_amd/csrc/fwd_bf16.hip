@@ -47,7 +47,7 @@ struct alignas(16) FwdLds {
     alignas(16) bf16 v[kStages][kTile * D];    // V tiles
 };
 
-template <int D>
+template <int D, bool SAVE>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     bf16x8 qhi[NCH], qlo[NCH];
     row_operands<D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D, cs,
                     min(qrow, T_ - 1), half, qhi, qlo);
+
     wait_vmcnt<0>();   // query operands and the first two tiles (see copy16_to_lds)
 
     // per-lane LDS offsets of the key row fragments (row 32*kt + col, chunks 2c + half)
@@ -226,6 +227,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
             }
         if (half == 0) a.lse[(size_t)bh * T_ + qrow] = (m_run + __log2f(l_tot)) * kLn2;
     }
+    if constexpr (SAVE) {
+        // the training forward keeps the rotated query for the backward, in the same two bf16
+        // parts (this lane's slots: d = 16 c + 8 half + 0..7); written last, so that these stores
+        // do not compete with the loads the first steps wait for
+        if (qrow < T_) {
+            const size_t off = ((size_t)bh * T_ + qrow) * D + 8 * half;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off + 16 * c) = qhi[c];
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off + 16 * c) = qlo[c];
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -233,7 +247,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 template <int D>
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     const long blocks = (long)((a.T + kQBlk - 1) / kQBlk) * a.B * a.Hq;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    if (a.qrot) hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@ struct FwdArgs {
     const float* rope_cs;   // [T][D/2][2] or nullptr (bf16 kernel: used for the queries only)
     int B, Hq, Hkv, T;
     float scale;
+    void* qrot;             // bf16 kernel, training variant: the rotated queries' hi and lo bf16
+    void* qrot_lo;          // parts as the backward reads them ([B, Hq, T, D] each), or nullptr
 };
 
 struct BwdArgs {
@@ -96,8 +98,11 @@ int proj_tile_tokens();
 hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+// a.qrot set: also writes the rotated queries (hi and lo parts) for the backward
 template <int D> hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream);
+// rotate == false: only the per-row (l', delta) data; the rotated queries and keys are already in
+// the workspace (written by the training forward)
+template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream, bool rotate = true);
 template <int D> hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D> hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 5
+#define NE_ABI_VERSION 6
 
 enum {
     NE_OK = 0,
@@ -148,6 +148,28 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
 int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, const void* v,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * The training pair: the same forward and backward as ne_attn_fwd / ne_attn_bwd (identical results,
+ * bit for bit), sharing one workspace (>= ne_attn_bwd_workspace_bytes(p), owned by the caller).
+ * ne_attn_fwd_train also leaves in it what the backward would otherwise recompute from q and k:
+ * on the bf16 path the rotated queries (as two bf16 parts) and the rotated keys.  The backward
+ * preprocess then reads only O, dO and L.  Between the two calls the workspace must not be used
+ * otherwise; q, k and the params must be the same.  On the float32 path the pair is ne_attn_fwd
+ * followed by ne_attn_bwd.  Arguments, layouts and errors as for ne_attn_fwd / ne_attn_bwd.
+ * (Keeping the forward's rotated operands for the backward instead of recomputing them: the
+ * saved-activation pattern of the FlashAttention backward the NanoEuler pages build on,
+ * agentlenshq NanoEuler page, "커널 구현".)
+ */
+int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+int ne_attn_bwd_train(const ne_attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+/* the first half of ne_attn_bwd_train (its second half is ne_attn_bwd_main) */
+int ne_attn_bwd_train_preprocess(const ne_attn_params* p, const void* q, const void* k, const void* o,
+                                 const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Decode-time attention: n new tokens per sequence against a KV cache (the token-by-token

@@ -50,6 +50,24 @@ def run_gpu(q, k, v, do, dtype, theta=10000.0, scale=None):
     return tuple(to_np(t) for t in (o, lse, dq, dk, dv))
 
 
+def run_gpu_train(q, k, v, do, dtype, theta=10000.0, scale=None):
+    """The same through the training pair (ne_attn_fwd_train / ne_attn_bwd_train, one workspace)."""
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
+    B, Hq, T, D = q.shape
+    cs = ne.rope_table(T, D, theta, qd.device) if theta and theta > 0 else None
+    p = ne.make_params(B, Hq, k.shape[1], T, D, ne._dtype_code(qd), scale, cs)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device=qd.device)
+    ws = torch.full((ne.bwd_workspace_bytes(p),), 0xFF, dtype=torch.uint8, device=qd.device)
+    ne.attn_fwd_train_into(p, qd, kd, vd, o, lse, ws)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    ne.attn_bwd_train_into(p, qd, kd, vd, o, lse, dod, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return tuple(to_np(t) for t in (o, lse, dq, dk, dv))
+
+
 def compare(gpu, ref, dtype, groups=None, Hq=None, Hkv=None):
     """Per-tensor relative errors; restricted to the (b, g) groups when given."""
     names = ("O", "L", "dQ", "dK", "dV")
@@ -69,8 +87,8 @@ def compare(gpu, ref, dtype, groups=None, Hq=None, Hkv=None):
     return errs
 
 
-def check(q, k, v, do, dtype, theta=10000.0, scale=None, groups=None, label=""):
-    gpu = run_gpu(q, k, v, do, dtype, theta, scale)
+def check(q, k, v, do, dtype, theta=10000.0, scale=None, groups=None, label="", train=False):
+    gpu = (run_gpu_train if train else run_gpu)(q, k, v, do, dtype, theta, scale)
     ref = oracle.attention(q, k, v, do, theta=theta, scale=scale, groups=groups)
     errs = compare(gpu, ref, dtype, groups, q.shape[1], k.shape[1])
     log_path = os.environ.get("NE_PARITY_LOG")
