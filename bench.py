@@ -44,7 +44,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (the default lets the clocks settle: ~40 ms of work)")
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (default: the 116M-model layer)")
     ap.add_argument("--decode", type=int, default=0, help="decode workload id 1..2 instead of the training step")
     ap.add_argument("--qkv", type=int, default=0, help="projection workload id (1) instead of the training step")

@@ -28,8 +28,9 @@
 //       queries 32w..32w+31, one lane per query.  Key/value tiles of 64 stream through LDS;
 //       S^T = K~ Q~^T and dP^T = V dO^T put one query per lane, and dQ^T += K~^T dS'^T takes
 //       dS'^T straight from the registers.  dQ is un-rotated and written once.
-//   Tiles reach LDS through the three-stage copy pipeline of tiles.hpp (buffer_load ... lds two
-//   steps ahead, swizzled unpadded tiles, one wait and one barrier per step).  Blocks are ordered
+//   Tiles reach LDS through the copy pipeline of tiles.hpp with two stages (buffer_load ... lds
+//   one step ahead, swizzled unpadded tiles, one wait and one barrier per step; a third stage
+//   measured no faster and costs 25 KB of LDS per dK/dV workgroup).  Blocks are ordered
 //   heaviest causal work first; tiles wholly above the diagonal are never visited.  The two roles
 //   recompute S and dP separately in exchange for having no cross-XCD float32 atomics, which on
 //   this machine go out to the memory fabric.
@@ -46,6 +47,7 @@ constexpr int kQBlk = 128;             // queries per dQ block
 constexpr int kThreads = kBlockThreads;
 constexpr int kWaves = kBlockWaves;
 constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
+constexpr int kBS = 2;                 // LDS stages: a tile is fetched one step before its use
 
 // (l', delta) of a 64-row query tile, stored in the workspace exactly as in LDS: 4 groups of 16
 // rows [l' x 16 | delta x 16] (512 bytes per tile); wave w copies group w with 8 lanes.
@@ -54,16 +56,16 @@ __device__ inline int ld_dlt(int q) { return (q >> 4) * 32 + 16 + (q & 15); }
 
 template <int D>
 struct alignas(16) DkdvLds {
-    alignas(16) bf16 q[kStages][kTile * D];    // Q~ tiles [query][d] (hi part)
-    alignas(16) bf16 ql[kStages][kTile * D];   // Q~ remainder tiles (lo part)
-    alignas(16) bf16 g[kStages][kTile * D];    // dO tiles
-    alignas(16) float ld[kStages][2 * kTile];  // l' and delta, see ld_lsc
+    alignas(16) bf16 q[kBS][kTile * D];    // Q~ tiles [query][d] (hi part)
+    alignas(16) bf16 ql[kBS][kTile * D];   // Q~ remainder tiles (lo part)
+    alignas(16) bf16 g[kBS][kTile * D];    // dO tiles
+    alignas(16) float ld[kBS][2 * kTile];  // l' and delta, see ld_lsc
 };
 
 template <int D>
 struct alignas(16) DqLds {
-    alignas(16) bf16 k[kStages][kTile * D];    // K~ tiles [key][d]
-    alignas(16) bf16 v[kStages][kTile * D];    // V tiles
+    alignas(16) bf16 k[kBS][kTile * D];    // K~ tiles [key][d]
+    alignas(16) bf16 v[kBS][kTile * D];    // V tiles
 };
 
 template <int D>
@@ -107,7 +109,6 @@ template <int D>
 __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
-    constexpr int kCopies = 3 * TileCopy<D>::NU + 1;   // copies per wave per step: 3 tiles + l'/delta
     const int T_ = a.T;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.Hq / a.Hkv;
@@ -152,8 +153,6 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     issue(0, 0, 0);
     int ih = 0, it = 1;                               // head / tile of the next step to issue
     if (it == nsph) { it = 0; ++ih; }
-    if (nsteps > 1) issue(ih, it, 1);
-    if (++it == nsph) { it = 0; ++ih; }
 
     // this lane's key row: K~ and V as B operands
     bf16x8 kop[NCH], vop[NCH];
@@ -167,7 +166,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
             vop[c] = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
         }
     }
-    wait_vmcnt<0>();   // operands and the first two tiles (see copy16_to_lds)
+    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the row fragments (query row 32*qh + col, chunks 2c + half)
     int roff[NCH];
@@ -180,11 +179,10 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 
     int buf = 0, ct = 0;                              // stage and query tile of the current step
     for (int st = 0; st < nsteps; ++st) {
-        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
-        else wait_vmcnt<0>();
-        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
-        if (st + 2 < nsteps) {
-            issue(ih, it, buf == 0 ? 2 : buf - 1);
+        wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
+        step_barrier();                      // tile st is complete; the other stage is free
+        if (st + 1 < nsteps) {
+            issue(ih, it, buf ^ 1);
             if (++it == nsph) { it = 0; ++ih; }
         }
         const bf16* Qs = S.q[buf];
@@ -244,7 +242,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                 }
             __builtin_amdgcn_s_setprio(0);
         }
-        buf = buf == kStages - 1 ? 0 : buf + 1;
+        buf ^= 1;
         if (++ct == nsph) ct = 0;
     }
 
@@ -295,7 +293,6 @@ template <int D>
 __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
-    constexpr int kCopies = 2 * TileCopy<D>::NU;     // copies per wave per step: K~ and V tiles
     const int T_ = a.T;
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
@@ -323,7 +320,6 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         tc.copy(rv, row0, lv + so, w);
     };
     issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
 
     // this lane's query row: Q~ (hi and lo) and dO as B operands, l' and delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
@@ -342,7 +338,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + rowc / kTile) * 2 * kTile;
     const float lsc = ldt[ld_lsc(rowc % kTile)];
     const float dlt = ldt[ld_dlt(rowc % kTile)];
-    wait_vmcnt<0>();   // operands and the first two tiles (see copy16_to_lds)
+    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
@@ -357,10 +353,9 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 
     int buf = 0;                                      // stage of the current step
     for (int st = 0; st < nsteps; ++st) {
-        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
-        else wait_vmcnt<0>();
-        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
-        if (st + 2 < nsteps) issue(st + 2, buf == 0 ? 2 : buf - 1);
+        wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
+        step_barrier();                      // tile st is complete; the other stage is free
+        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
         const int j0 = st * kTile;
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
@@ -431,7 +426,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                 for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
             __builtin_amdgcn_s_setprio(0);
         }
-        buf = buf == kStages - 1 ? 0 : buf + 1;
+        buf ^= 1;
     }
 
     // dQ = R^T dQ~ ; lane owns one query, 4 consecutive d per register group

@@ -1,7 +1,8 @@
 // tiles.hpp -- LDS tile staging and operand helpers shared by the bf16 kernels (gfx950).
 //
 // Tiles of 64 rows x D bf16 go from global memory straight into LDS (buffer_load_dwordx4 ... lds:
-// no registers, no LDS store instructions) through three stages, two steps ahead of their use.
+// no registers, no LDS store instructions) through kStages stages, two steps ahead of their use
+// (the backward uses two stages, one step ahead).
 // LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (Swz) so that row reads
 // (ds_read_b128) and transposed reads (ds_read_b64_tr_b16) stay conflict-free.  A step opens with
 // an explicit wait for this wave's copies of the current tile and one barrier without a fence.
@@ -110,7 +111,10 @@ __device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(l
 // per-lane operands a kernel loads before its step loop are waited for (vmcnt(0)) before the loop
 // starts, so no other vector-memory load is in flight in it.
 __device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+    // soff and lds are wave-uniform; readfirstlane puts them in scalar registers even where the
+    // compiler kept a uniform value in a vector register
+    const unsigned so = __builtin_amdgcn_readfirstlane(soff), m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(so), "{m0}"(m0)
                  : "memory");
 }
 

@@ -150,8 +150,10 @@ int ne_attn_bwd_main(const ne_attn_params* p, const void* q, const void* k, cons
                      size_t workspace_bytes, void* stream);
 
 /*
- * The training pair: the same forward and backward as ne_attn_fwd / ne_attn_bwd (identical results,
- * bit for bit), sharing one workspace (>= ne_attn_bwd_workspace_bytes(p), owned by the caller).
+ * The training pair: the same forward and backward as ne_attn_fwd / ne_attn_bwd, sharing one
+ * workspace (>= ne_attn_bwd_workspace_bytes(p), owned by the caller).  o and lse are identical
+ * bit for bit; the gradients agree up to float32 rounding (the rotation of q is evaluated by
+ * another kernel, whose products the compiler contracts differently).
  * ne_attn_fwd_train also leaves in it what the backward would otherwise recompute from q and k:
  * on the bf16 path the rotated queries (as two bf16 parts) and the rotated keys.  The backward
  * preprocess then reads only O, dO and L.  Between the two calls the workspace must not be used
