@@ -172,6 +172,10 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     int roff[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) roff[c] = Swz<D>::at(32 * qh + col, 16 * c + 8 * half);
+    // per-lane bases of the transposed dO / Q~ fragment reads (rows of this wave's query half)
+    int trb[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) trb[dt] = tr_base<D>(32 * dt, lane) + 32 * qh * D;
 
     f32x16 dkt[NDT], dvt[NDT];
 #pragma unroll
@@ -217,14 +221,12 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 gt[2][NDT], qtf[2][NDT];
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc) {
-                const int kb0 = 32 * qh + 16 * pc + 4 * half;
+            for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    gt[pc][dt] = tr_frag_swz<D>(Gs, 32 * dt, kb0, kb0 + 8, lane);
-                    qtf[pc][dt] = tr_frag_swz<D>(Qs, 32 * dt, kb0, kb0 + 8, lane);
+                    gt[pc][dt] = tr_frag_at<D>(Gs, trb[dt], 16 * pc);
+                    qtf[pc][dt] = tr_frag_at<D>(Qs, trb[dt], 16 * pc);
                 }
-            }
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 pb[2], sb[2];
             if (first && kh == qh)
@@ -346,6 +348,10 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) roff[kt][c] = Swz<D>::at(32 * kt + col, 16 * c + 8 * half);
+    // per-lane bases of the transposed K~ fragment reads (one per 32 columns of d)
+    int ktb[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) ktb[dt] = tr_base<D>(32 * dt, lane);
 
     f32x16 dqt[NDT];
 #pragma unroll
@@ -391,11 +397,9 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 ktf[4][NDT];
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
+            for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_swz<D>(Ks, 32 * dt, kb0, kb0 + 8, lane);
-            }
+                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_at<D>(Ks, ktb[dt], 16 * pc);
             __builtin_amdgcn_sched_barrier(0);
             // dS'^T = P' (dP^T - delta), packed as B operands (4 chunks of 16 keys)
             bf16x8 sb[4];

@@ -117,6 +117,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) roff[kt][c] = Swz<D>::at(32 * kt + col, 16 * c + 8 * half);
+    // per-lane bases of the transposed V fragment reads (one per 32 columns of d)
+    int vtb[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vtb[dt] = tr_base<D>(32 * dt, lane);
 
     f32x16 oacc[NDT];
 #pragma unroll
@@ -157,11 +161,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 vf[4][NDT];
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const int kb0 = 32 * (pc >> 1) + 16 * (pc & 1) + 4 * half;
+            for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag_swz<D>(Vs, 32 * dt, kb0, kb0 + 8, lane);
-            }
+                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag_at<D>(Vs, vtb[dt], 16 * pc);
             __builtin_amdgcn_sched_barrier(0);
             if (j0 + kTile - 1 > wq0) {     // diagonal tile for this wave: keys after the query
 #pragma unroll

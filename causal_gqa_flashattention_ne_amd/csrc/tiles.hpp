@@ -69,6 +69,24 @@ __device__ inline bf16x8 tr_frag_swz(const bf16* X, int m0, int kb0, int kb1, in
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same fragment with the address split into a per-lane base and a row block known at compile
+// time.  The swizzle f(r) depends on r mod 8 only, so moving 8 rows down moves every chunk by 8 * D
+// elements: tr_base gives the lane's element offset for the columns m0.. at rows 4 * half + s / 4,
+// and tr_frag_at reads rows r0 + that and r0 + 8 + that (r0 a multiple of 8), the same values as
+// tr_frag_swz(X, m0, r0 + 4 * half, r0 + 8 + 4 * half, lane) with only an immediate offset added.
+template <int D>
+__device__ inline int tr_base(int m0, int lane) {
+    const int s = lane & 15;
+    const int m = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    return Swz<D>::at(4 * (lane >> 5) + (s >> 2), m);
+}
+template <int D>
+__device__ inline bf16x8 tr_frag_at(const bf16* X, int base, int r0) {
+    const bf16x4 lo = tr_read(X + base + r0 * D);
+    const bf16x4 hi = tr_read(X + base + (r0 + 8) * D);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima: no wait on them).  The empty asm
 // keeps the compiler from moving the LDS reads of the tile waited for above the wait.
 template <int N>
