@@ -7,8 +7,11 @@
 // A workgroup owns 128 queries of one (batch, query head); wave w owns queries 32w..32w+31,
 // one lane per query.  The keys arrive already rotated (K~ = R k, written once per call by the
 // RoPE kernel, so no query head of a group rotates them again).  Key/value tiles of 64 rows reach
-// LDS through the three-stage copy pipeline of tiles.hpp (buffer_load ... lds two steps ahead of
-// use, swizzled unpadded tiles).  Only tiles at or before the block's last query are visited.
+// LDS through the copy pipeline of tiles.hpp with two stages (buffer_load ... lds one step ahead
+// of use, swizzled unpadded tiles).  Only tiles at or before the block's last query are visited.
+// Each step works in two 32-key halves (key fragments, then P^T and the V^T fragments of the PV
+// product), so that the fragments of only one half are live at a time: with two stages this
+// keeps three workgroups per CU at head_dim 64 and makes two fit at 128.
 //   S^T = K~ Q~^T        (A = key rows from LDS, B = this lane's rotated query in registers,
 //                         split into bf16 hi + lo so that only the keys' rounding enters S)
 //   P^T = exp2(S^T * scale*log2(e) - m)
@@ -27,6 +30,10 @@ namespace ne {
 namespace {
 
 constexpr int kTile = kTileRows;       // keys per step
+constexpr int kFS = 2;                 // LDS stages: a tile is fetched one step before its use
+// workgroups per CU the kernel is compiled for (registers: 133 at head_dim 64, 219 at 128)
+template <int D> struct FwdOcc { static constexpr int MINB = 3; };
+template <> struct FwdOcc<128> { static constexpr int MINB = 2; };
 constexpr int kQBlk = 128;             // queries per workgroup
 constexpr int kThreads = kBlockThreads;
 constexpr float kRescale = 8.f;        // log2 units of headroom before the running max is moved
@@ -43,15 +50,14 @@ __device__ inline float partner_sum(float x) {
 
 template <int D>
 struct alignas(16) FwdLds {
-    alignas(16) bf16 k[kStages][kTile * D];    // K~ tiles [key][d] (swizzled)
-    alignas(16) bf16 v[kStages][kTile * D];    // V tiles
+    alignas(16) bf16 k[kFS][kTile * D];    // K~ tiles [key][d] (swizzled)
+    alignas(16) bf16 v[kFS][kTile * D];    // V tiles
 };
 
 template <int D, bool SAVE>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, FwdOcc<D>::MINB) void fwd_bf16_kernel(FwdArgs a) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
-    constexpr int kCopies = 2 * TileCopy<D>::NU;      // copies per wave per step: K~ and V tiles
     __shared__ FwdLds<D> S;
 
     const int T_ = a.T;
@@ -100,7 +106,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         tc.copy(rv, row0, lv + so, w);
     };
     issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
 
     // this lane's query, rotated in float32 and held as two bf16 B operands (hi + lo) of
     // S^T = K~ Q~^T: the rotated query is then exact to ~2^-16 in the score product, and only the
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     row_operands<D>(reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D, cs,
                     min(qrow, T_ - 1), half, qhi, qlo);
 
-    wait_vmcnt<0>();   // query operands and the first two tiles (see copy16_to_lds)
+    wait_vmcnt<0>();   // query operands and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the key row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
@@ -130,41 +135,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     int buf = 0;                                      // stage of the current step
     for (int st = 0; st < nsteps; ++st) {
-        if (st + 1 < nsteps) wait_vmcnt<kCopies>();
-        else wait_vmcnt<0>();
-        step_barrier();                      // tile st is complete; stage (st + 2) % 3 is free
-        if (st + 2 < nsteps) issue(st + 2, buf == 0 ? 2 : buf - 1);
+        wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
+        step_barrier();                      // tile st is complete; the other stage is free
+        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
         const int j0 = st * kTile;
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
-            // key fragments as one batch, then the two independent accumulation chains interleaved;
-            // the V^T fragments of the PV product are read while the softmax waits for S
-            bf16x8 kf[2][NCH];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) kf[kt][c] = *reinterpret_cast<const bf16x8*>(Ks + roff[kt][c]);
-            __builtin_amdgcn_sched_barrier(0);
+            // per 32-key half: its key fragments as one batch, then one accumulation chain (dependent
+            // MFMAs issue back to back on gfx950, so the halves need not be interleaved)
             f32x16 sT[2];
-            sT[0] = M::mma(kf[0][0], qhi[0], f32x16{});
-            sT[1] = M::mma(kf[1][0], qhi[0], f32x16{});
-            sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
-            sT[1] = M::mma(kf[1][0], qlo[0], sT[1]);
 #pragma unroll
-            for (int c = 1; c < NCH; ++c) {
-                sT[0] = M::mma(kf[0][c], qhi[c], sT[0]);
-                sT[1] = M::mma(kf[1][c], qhi[c], sT[1]);
-                sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
-                sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
+            for (int kt = 0; kt < 2; ++kt) {
+                bf16x8 kf[NCH];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(Ks + roff[kt][c]);
+                __builtin_amdgcn_sched_barrier(0);
+                sT[kt] = M::mma(kf[0], qhi[0], f32x16{});
+                sT[kt] = M::mma(kf[0], qlo[0], sT[kt]);
+#pragma unroll
+                for (int c = 1; c < NCH; ++c) {
+                    sT[kt] = M::mma(kf[c], qhi[c], sT[kt]);
+                    sT[kt] = M::mma(kf[c], qlo[c], sT[kt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 vf[4][NDT];
-#pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) vf[pc][dt] = tr_frag_at<D>(Vs, vtb[dt], 16 * pc);
-            __builtin_amdgcn_sched_barrier(0);
             if (j0 + kTile - 1 > wq0) {     // diagonal tile for this wave: keys after the query
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
@@ -186,11 +181,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                 for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
                 m_run = m_new;
             }
-            // P^T (B operands, 4 chunks of 16 keys in accumulator order) and the row sum
-            bf16x8 pb[4];
+            // per 32-key half: V^T fragments, P^T (B operands, 2 chunks of 16 keys) and the row sum,
+            // then O^T += V^T P^T
             float ls = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) {
+                bf16x8 vf[2][NDT];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) vf[h2][dt] = tr_frag_at<D>(Vs, vtb[dt], 32 * kt + 16 * h2);
+                bf16x8 pb[2];
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     float p[4];
@@ -200,18 +201,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                         ls += p[e];
                     }
                     const bf16x4 p4 = cvt4(p);
-                    const int pc = 2 * kt + (rg >> 1);
-                    if (rg & 1) pb[pc] = __builtin_shufflevector(pb[pc].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    else pb[pc] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    if (rg & 1) pb[rg >> 1] = __builtin_shufflevector(pb[rg >> 1].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    else pb[rg >> 1] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::mma(vf[h2][dt], pb[h2], oacc[dt]);
+            }
             l_run += ls;
-            // O^T += V^T P^T
-#pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::mma(vf[pc][dt], pb[pc], oacc[dt]);
         }
-        buf = buf == kStages - 1 ? 0 : buf + 1;
+        buf ^= 1;
     }
 
     // epilogue: O = O^T / l, L = (m + log2 l) ln 2

@@ -1,8 +1,8 @@
 // tiles.hpp -- LDS tile staging and operand helpers shared by the bf16 kernels (gfx950).
 //
 // Tiles of 64 rows x D bf16 go from global memory straight into LDS (buffer_load_dwordx4 ... lds:
-// no registers, no LDS store instructions) through kStages stages, two steps ahead of their use
-// (the backward uses two stages, one step ahead).
+// no registers, no LDS store instructions) through LDS stages: kStages (three, tiles two steps
+// ahead of their use) in decode, two (one step ahead) in the forward and backward.
 // LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (Swz) so that row reads
 // (ds_read_b128) and transposed reads (ds_read_b64_tr_b16) stay conflict-free.  A step opens with
 // an explicit wait for this wave's copies of the current tile and one barrier without a fence.
@@ -15,7 +15,7 @@ namespace ne {
 constexpr int kTileRows = 64;                   // rows of one staged tile
 constexpr int kBlockThreads = 256;              // threads of every bf16 attention workgroup
 constexpr int kBlockWaves = kBlockThreads / 64;
-constexpr int kStages = 3;                      // LDS stages: a tile is fetched two steps before its use
+constexpr int kStages = 3;                      // decode's LDS stages: a tile is fetched two steps before its use
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
