@@ -9,11 +9,13 @@
 // row read of an LDS tile (8 consecutive k per lane, no transposes).  The product is formed
 // feature-major, Y^T = W X^T: a lane of a 32 x 32 x 16 MFMA result holds one token and, per group
 // of four registers, four consecutive features, so each RoPE pair sits in one lane.  A workgroup
-// (4 waves, 2 x 2) owns 128 features x 128 tokens; k advances 64 per step through two LDS stages
-// filled by buffer loads straight into LDS (tiles.hpp), one step ahead; at 64 KiB two workgroups
-// share a CU and overlap each other's waits (measured faster than three or four stages with one
-// workgroup per CU, and than 64- or 256-token tiles).  Results go through padded LDS rows to
-// 16-byte stores, each a run of 8 features of one (head, token) row.
+// (4 waves, 2 x 2) owns 128 features x 192 tokens; k advances 64 per step through two LDS stages
+// filled by buffer loads straight into LDS (tiles.hpp), one step ahead; at 80 KiB two workgroups
+// share a CU and overlap each other's waits.  192 tokens make the 116M model's projection
+// (8192 tokens x 1280 features) 430 tiles, one round of two workgroups on every CU: 128-token
+// tiles (640) needed a second round for the last quarter, which measured 9% slower; three or four
+// stages, k = 32 steps and three workgroups per CU measured no faster.  Results go through padded
+// LDS rows to 16-byte stores, each a run of 8 features of one (head, token) row.
 //
 // Placement: workgroup i runs on XCD i % 8.  Each XCD takes a contiguous range of tiles in
 // token-major order (features fastest), so the feature tiles of one token tile run back to back
@@ -28,10 +30,10 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kFeat = 128;                 // features per output tile
-constexpr int kWT = 2;                     // 32-token MFMA tiles per wave along tokens
+constexpr int kWT = 3;                     // 32-token MFMA tiles per wave along tokens
 constexpr int kTok = 2 * 32 * kWT;         // tokens per output tile
 constexpr int kK = 64;                     // k per step
-constexpr int kStagesP = 2;               // 64 KiB of LDS: two workgroups per CU
+constexpr int kStagesP = 2;               // 80 KiB of LDS: two workgroups per CU
 constexpr int kCPR = kK / 8;               // 16-byte chunks per tile row
 
 struct alignas(16) ProjLds {
@@ -41,6 +43,7 @@ struct alignas(16) ProjLds {
 // epilogue staging: [token][feature] bf16 rows padded by 8 elements (conflict-free 8-byte writes)
 constexpr int kOutPitch = kFeat + 8;
 static_assert(kTok * kOutPitch * 2 <= (int)sizeof(ProjLds), "output staging must fit in the stage buffers");
+static_assert(2 * sizeof(ProjLds) <= 160 * 1024, "two workgroups per CU");
 
 // Copies of ROWS x 64 bf16 tiles of a row-major matrix with a row pitch of `pitch` bytes into
 // swizzled LDS tiles, by the 4 waves of a workgroup (the tile copy of tiles.hpp with a run-time
@@ -75,7 +78,7 @@ __device__ inline void divmod(int m, int d, double inv_d, int& q, int& r) {
 }
 
 template <bool ROPE>
-__global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
+__global__ __launch_bounds__(kBlockThreads, 2) void proj_kernel(ProjArgs a) {
     using M = Mfma<bf16>;
     using CW = PitchCopy<kFeat>;
     using CX = PitchCopy<kTok>;
@@ -114,14 +117,14 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int i = 0; i < kStagesP - 1; ++i)
         if (i < nk) issue(i);
-    // every table entry this lane needs, loaded right after the first tiles are requested and
-    // pinned here: the compiler's wait for them (vmcnt 0) then also covers those tiles, whose
-    // latency it overlaps, and no copy is in flight behind it
+    // every table entry this lane needs, loaded as one batch after the main loop (no copy is in
+    // flight then) and pinned, so that the compiler waits once for all of them; held through the
+    // loop they would cost 96 registers
     f32x4 cs[2][kWT][4];
     bool rot[2];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb) rot[fb] = ROPE && n0 + wf * 64 + fb * 32 < nqk;   // whole 32-blocks
-    if constexpr (ROPE) {
+    auto load_cs = [&]() {
 #pragma unroll
         for (int tb = 0; tb < kWT; ++tb) {
             const int m = m0 + wt * 32 * kWT + tb * 32 + col;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
             for (int tb = 0; tb < kWT; ++tb)
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) asm volatile("" : "+v"(cs[fb][tb][rq]));
-    }
+    };
 
 
     int ra[2][4], rb[kWT][4];                       // fragment offsets: [block][k chunk of 16]
@@ -186,6 +189,7 @@ __global__ __launch_bounds__(kBlockThreads) void proj_kernel(ProjArgs a) {
     }
 
     // ---- epilogue: RoPE on query and key features, bf16, staged through LDS ----
+    if constexpr (ROPE) load_cs();
     __syncthreads();                                // every wave is done with the stage buffers
     bf16* out = reinterpret_cast<bf16*>(&S);
 #pragma unroll
