@@ -253,3 +253,16 @@ class QkvWorkload:
 QKV_WORKLOADS = {
     1: QkvWorkload("gpt116m-qkv-proj-bf16", 16, 512, 768, 12, 4, 64, seed=21),
 }
+
+
+def device_normals(seed: int, shape, device, dtype, sigma: float = 1.0):
+    """Normals of standard deviation ``sigma`` drawn on ``device`` by torch's seeded generator
+    (Philox4x32-10 on GPUs), in ``dtype``: for tensors too large to draw on the host.  A check that
+    uses them reads back the slices it compares, so both sides see the same values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=dtype)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x
