@@ -1,12 +1,13 @@
-"""GPU parity at the largest attention shape the C ABI accepts.
+"""GPU parity at the largest shapes the C ABI accepts.
 
-A [B, Hq, T, D] tensor may hold at most 2^31 - 1 elements; here the query, output and gradient
-tensors hold 2^31 - 32768 (B = 65535, Hq = 8, Hkv = 2, T = 64, D = 64, bf16, RoPE on), so every
-element offset, grid size and per-row index of the forward, the backward and the training pair
-runs near the top of its range (about 30 GB of buffers).  Inputs are drawn on the device
-(gen.device_normals); the first, a middle and the last kv group (all their query heads and
-positions) are read back and compared with the oracle at the bf16 bar, relative to each
-output's largest magnitude within the group.
+A tensor passed to the library may hold at most 2^31 - 1 elements.  Attention: the query, output
+and gradient tensors hold 2^31 - 32768 (B = 65535, Hq = 8, Hkv = 2, T = 64, D = 64, bf16, RoPE
+on), so every element offset, grid size and per-row index of the forward, the backward and the
+training pair runs near the top of its range (about 50 GB of buffers); decode: caches of
+2^31 - 16384 elements; projection: x and the outputs near 2^31 elements.  Inputs are drawn on the
+device (gen.device_normals); slices at the start, the middle and the end are read back and
+compared with the oracle at each path's bar, relative to each output's largest magnitude within
+the slice.
 """
 import sys
 
@@ -69,3 +70,53 @@ def test_max_elements_bf16_forward_backward_and_training_pair():
     assert torch.equal(o2, o) and torch.equal(lse2, lse)
     del o, lse, dq, dk, dv
     check_groups(q, k, v, do, o2, lse2, dq2, dk2, dv2, "training pair")
+
+
+def test_max_cache_decode():
+    """Decode against caches of 2^31 - 16384 elements each (64 sequences, 4 kv heads, 131071
+    rows of 64): valid lengths from 1 to the full cache; the first, a middle and the last
+    sequence checked against the oracle (all 12 query heads)."""
+    Bd, Hq, Hkv, n, Dd, rows = 64, 12, 4, 1, 64, 131071
+    assert Bd * Hkv * rows * Dd == (1 << 31) - 16384
+    dev = torch.device("cuda:0")
+    q = gen.device_normals(71, (Bd, Hq, n, Dd), dev, torch.bfloat16)
+    kc = gen.device_normals(72, (Bd, Hkv, rows, Dd), dev, torch.bfloat16)
+    vc = gen.device_normals(73, (Bd, Hkv, rows, Dd), dev, torch.bfloat16)
+    lens = np.random.default_rng(74).integers(1, rows + 1, size=Bd)
+    lens[0], lens[Bd // 2], lens[-1] = rows, 1, rows - 37
+    kv_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    o, lse = ne.attn_decode(q, kc, vc, kv_len)
+    torch.cuda.synchronize()
+    for b in (0, Bd // 2, Bd - 1):
+        L = int(lens[b])
+        qs = q[b:b + 1].float().cpu().numpy().astype(np.float64)
+        ks = kc[b:b + 1, :, :L].float().cpu().numpy().astype(np.float64)
+        vs = vc[b:b + 1, :, :L].float().cpu().numpy().astype(np.float64)
+        ro, rl = oracle.decode(qs, ks, vs, np.array([L]), theta=10000.0)
+        eo = rel_err(o[b:b + 1].float().cpu().numpy(), ro)
+        el = rel_err(lse[b:b + 1].cpu().numpy(), rl)
+        log("decode sequence %d (%d rows): e(o) %.2e e(L) %.2e" % (b, L, eo, el))
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"], (b, eo, el)
+
+
+def test_max_tokens_projection():
+    """The projection with 2795520 tokens of width 768 into 768 features (x and the outputs near
+    2^31 elements; the largest token count the ABI accepts at this width, to within one tile),
+    three batch rows checked against the oracle at the projection's bar (fp32 accumulation and
+    one bf16 rounding: 4e-3)."""
+    Bp, Tp, C, Hq, Hkv, Dp = 5460, 512, 768, 8, 2, 64
+    N = (Hq + 2 * Hkv) * Dp
+    M = Bp * Tp
+    assert M * N < (1 << 31) and (M + 192) * C < (1 << 31)     # 192: the kernel's token tile
+    dev = torch.device("cuda:0")
+    x = gen.device_normals(81, (Bp, Tp, C), dev, torch.bfloat16)
+    w = gen.device_normals(82, (N, C), dev, torch.bfloat16, sigma=C ** -0.5)
+    q, k, v = ne.qkv_proj(x, w, Hq, Hkv, rope_theta=10000.0)
+    torch.cuda.synchronize()
+    wn = w.float().cpu().numpy().astype(np.float64)
+    for b in (0, Bp // 2, Bp - 1):
+        xs = x[b:b + 1].float().cpu().numpy().astype(np.float64)
+        ref = oracle.qkv_proj(xs, wn, Hq, Hkv, theta=10000.0)
+        errs = [rel_err(g[b:b + 1].float().cpu().numpy(), r) for g, r in zip((q, k, v), ref)]
+        log("projection batch row %d: e(q) %.2e e(k) %.2e e(v) %.2e" % (b, *errs))
+        assert max(errs) <= 4e-3, (b, errs)
