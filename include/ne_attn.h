@@ -20,8 +20,8 @@
  *    by ne_rope_table (cos/sin evaluated in double, stored as float32).
  *  * Scores S_ij = scale * <R_i q_i, R_j k_j>; lse_i = ln sum_{j<=i} exp(S_ij) (natural log).
  *  * Element types: NE_DTYPE_F32 (float32 in/out, float32 arithmetic) or NE_DTYPE_BF16 (bfloat16
- *    in/out, bf16 matrix-core products with float32 accumulation).  lse and the workspace are
- *    always float32.
+ *    in/out, bf16 matrix-core products with float32 accumulation).  lse is always float32; a
+ *    workspace is opaque bytes whose size the matching *_workspace_bytes() call gives.
  *  * Memory: every pointer is device memory owned by the caller, 16-byte aligned.  The library
  *    allocates nothing and keeps no state beyond a cached device-property query.  Inputs are
  *    never written; outputs are fully overwritten (never accumulated into).
@@ -112,7 +112,9 @@ size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p);
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of float32 workspace that ne_attn_bwd needs for these parameters (0 on a bad shape). */
+/* Bytes of workspace that ne_attn_bwd needs for these parameters (0 on a bad shape): float32,
+ * delta and a float32 dQ accumulator; bf16, the per-row exponent offsets and deltas, the rotated
+ * queries (two bf16 parts) and the rotated keys. */
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);
 
 /*
