@@ -366,8 +366,11 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
             const bf16* Vs = S.v[buf];
-            // key / value row fragments as one batch, then four independent chains interleaved;
-            // the transposed K~ fragments of the dQ product are read while the softmax waits
+            // key / value row fragments as one batch.  Then per 32-key half (kt) its score and dP
+            // products; L and delta are known, so a half's dS' needs only its own products: the
+            // softmax of half 0 is slotted between the products of half 1, and that of half 1
+            // between the dQ products of half 0, so that vector work and matrix products of one
+            // wave overlap
             bf16x8 kf[2][NCH], vf[2][NCH];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -377,23 +380,16 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                     vf[kt][c] = *reinterpret_cast<const bf16x8*>(Vs + roff[kt][c]);
                 }
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
             f32x16 sT[2], dpT[2];
+            sT[0] = M::mma(kf[0][0], qop[0], f32x16{});
+            dpT[0] = M::mma(vf[0][0], gop[0], f32x16{});
+            sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                sT[kt] = M::mma(kf[kt][0], qop[0], f32x16{});
-                dpT[kt] = M::mma(vf[kt][0], gop[0], f32x16{});
-                sT[kt] = M::mma(kf[kt][0], qlo[0], sT[kt]);
+            for (int c = 1; c < NCH; ++c) {
+                sT[0] = M::mma(kf[0][c], qop[c], sT[0]);
+                dpT[0] = M::mma(vf[0][c], gop[c], dpT[0]);
+                sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
             }
-#pragma unroll
-            for (int c = 1; c < NCH; ++c)
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    sT[kt] = M::mma(kf[kt][c], qop[c], sT[kt]);
-                    dpT[kt] = M::mma(vf[kt][c], gop[c], dpT[kt]);
-                    sT[kt] = M::mma(kf[kt][c], qlo[c], sT[kt]);
-                }
-            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 ktf[4][NDT];
 #pragma unroll
@@ -401,34 +397,50 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_at<D>(Ks, ktb[dt], 16 * pc);
             __builtin_amdgcn_sched_barrier(0);
-            // dS'^T = P' (dP^T - delta), packed as B operands (4 chunks of 16 keys)
+            // dS'^T = P' (dP^T - delta) of register group rg of half kt, packed into the B operand
+            // chunk 2 kt + rg / 2 (4 chunks of 16 keys)
             bf16x8 sb[4];
             const bool diag = j0 + kTile - 1 > wq0;
+            auto ds_group = [&](int kt, int rg) {
+                float d[4];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    float d[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * rg + e;
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[kt][r], sl2, -lsc));
-                        if (diag && j0 + 32 * kt + acc_row(r, half) > qrow) p = 0.f;
-                        d[e] = p * (dpT[kt][r] - dlt);
-                    }
-                    const bf16x4 d4 = cvt4(d);
-                    const int pc = 2 * kt + (rg >> 1);
-                    if (rg & 1) sb[pc] = __builtin_shufflevector(sb[pc].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rg + e;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[kt][r], sl2, -lsc));
+                    if (diag && j0 + 32 * kt + acc_row(r, half) > qrow) p = 0.f;
+                    d[e] = p * (dpT[kt][r] - dlt);
                 }
-            // dQ~^T (D x 32 queries) += K~^T dS'^T  (K = the tile's keys, accumulator order)
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
+                const bf16x4 d4 = cvt4(d);
+                const int pc = 2 * kt + (rg >> 1);
+                if (rg & 1) sb[pc] = __builtin_shufflevector(sb[pc].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            // products of half 1, chunk by chunk, each followed by its share of half 0's groups
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
+            for (int c = 0; c < NCH; ++c) {
+                sT[1] = M::mma(kf[1][c], qop[c], c == 0 ? f32x16{} : sT[1]);
+                dpT[1] = M::mma(vf[1][c], gop[c], c == 0 ? f32x16{} : dpT[1]);
+                sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rg = c * 4 / NCH; rg < (c + 1) * 4 / NCH; ++rg) ds_group(0, rg);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // dQ~^T (D x 32 queries) += K~^T dS'^T (K = the tile's keys, accumulator order): the
+            // chunks of half 0, each followed by two of half 1's groups, then those of half 1
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
-            __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                ds_group(1, 2 * pc);
+                ds_group(1, 2 * pc + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int pc = 2; pc < 4; ++pc)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
         }
         buf ^= 1;
     }
