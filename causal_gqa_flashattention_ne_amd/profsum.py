@@ -7,6 +7,10 @@
         --pmc WRITE_SIZE) of `bench.py --copy-calibration`, each scaled by what the same counter
         reads for the calibration copy (256 MiB read + 256 MiB written per launch), tagged with a
         hash of each kernel's sources so that the benchmark stops quoting it once that kernel changes.
+    python -m causal_gqa_flashattention_ne_amd.profsum counters <dir> [<dir> ...]
+        per-kernel averages over dispatches of every counter or derived metric in the
+        counter_collection.csv files of one or more --pmc runs (e.g. MfmaUtil, MfmaFlopsBF16,
+        VALUBusy, LdsUtil, LDSBankConflict, OccupancyPercent).
 """
 import collections
 import csv
@@ -77,6 +81,21 @@ def traffic(fetch_dir, write_dir, out):
     print(json.dumps(res, indent=1))
 
 
+def counters(dirs):
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for k in vals.values() for c in k})
+    print("%-40s" % "kernel" + "".join("%17s" % c[:16] for c in names))
+    for kname, cs in vals.items():
+        short = next((v for key, v in KERNELS.items() if key + "<" in kname or ("::" + key + "(") in kname
+                      or kname.endswith(key) or key in kname), kname[:40])
+        print("%-40s" % short[:40] + "".join("%17.4g" % (sum(cs[c]) / len(cs[c])) if cs.get(c) else "%17s" % "-"
+                                            for c in names))
+
+
 def rows_from_db(path):
     c = sqlite3.connect(path)
     q = ("select name, count(*), avg(end-start)/1000.0, min(end-start)/1000.0, max(end-start)/1000.0, "
@@ -103,5 +122,7 @@ def main(path):
 if __name__ == "__main__":
     if sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "counters":
+        counters(sys.argv[2:])
     else:
         main(sys.argv[1])
