@@ -38,6 +38,7 @@ constexpr int kQBlk = 128;             // queries per workgroup
 constexpr int kThreads = kBlockThreads;
 constexpr float kRescale = 8.f;        // log2 units of headroom before the running max is moved
 constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
+constexpr int kSaveStep = 2;           // step after whose tile copies the training forward stores Q~
 
 __device__ inline float partner_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -138,6 +139,21 @@ __global__ __launch_bounds__(kThreads, FwdOcc<D>::MINB) void fwd_bf16_kernel(Fwd
         wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
         step_barrier();                      // tile st is complete; the other stage is free
         if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+        if constexpr (SAVE) {
+            // the training forward keeps the rotated query for the backward, in the same two bf16
+            // parts (this lane's slots: d = 16 c + 8 half + 0..7).  Stored once, right after the
+            // copies of step kSaveStep (or of the last step of a shorter block): issued before the
+            // first tiles they would delay them, and after the epilogue they would lengthen the
+            // tail of the blocks with the most steps
+            if (st == min(kSaveStep, nsteps - 1) && qrow < T_) {
+                const size_t off = ((size_t)bh * T_ + qrow) * D + 8 * half;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off + 16 * c) = qhi[c];
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off + 16 * c) = qlo[c];
+                }
+            }
+        }
         const int j0 = st * kTile;
         if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
             const bf16* Ks = S.k[buf];
@@ -228,19 +244,6 @@ __global__ __launch_bounds__(kThreads, FwdOcc<D>::MINB) void fwd_bf16_kernel(Fwd
                 *reinterpret_cast<bf16x4*>(o + 32 * dt + acc_row(r, half)) = cvt4(x);
             }
         if (half == 0) a.lse[(size_t)bh * T_ + qrow] = (m_run + __log2f(l_tot)) * kLn2;
-    }
-    if constexpr (SAVE) {
-        // the training forward keeps the rotated query for the backward, in the same two bf16
-        // parts (this lane's slots: d = 16 c + 8 half + 0..7); written last, so that these stores
-        // do not compete with the loads the first steps wait for
-        if (qrow < T_) {
-            const size_t off = ((size_t)bh * T_ + qrow) * D + 8 * half;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off + 16 * c) = qhi[c];
-                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off + 16 * c) = qlo[c];
-            }
-        }
     }
 }
 
