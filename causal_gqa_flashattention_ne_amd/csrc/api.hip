@@ -296,10 +296,11 @@ int ne_qkv_proj(const ne_qkv_params* p, const void* x, const void* w, void* q, v
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
-    // float32: delta | float32 dQ accumulator
+    // float32: delta | float32 dQ accumulator | dK and dV slices, one per share of a key tile
     // bf16: (l', delta) per row | rotated Q hi | rotated Q lo | rotated K
     if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
-    return delta_bytes(p) + qe * sizeof(float);
+    const size_t ns = (size_t)ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
+    return delta_bytes(p) + (qe + 2 * ns * ke) * sizeof(float);
 }
 
 namespace {
@@ -313,9 +314,12 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
     float* delta = nullptr;
     float* ld = nullptr;
     float* dq_acc = nullptr;
+    float* dk_acc = nullptr;
+    float* dv_acc = nullptr;
     void* qrot = nullptr;
     void* qrot_lo = nullptr;
     void* krot = nullptr;
+    int nsplit = 1;
     if (p->dtype == NE_DTYPE_BF16) {
         const size_t qb = (qe * 2 + 255) & ~(size_t)255;
         ld = reinterpret_cast<float*>(ws);
@@ -324,10 +328,14 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
         krot = ws + delta_bytes(p) + 2 * qb;
     } else {
         delta = reinterpret_cast<float*>(ws);
+        const size_t ke = (size_t)p->B * p->Hkv * p->T * p->D;
+        nsplit = ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
         dq_acc = reinterpret_cast<float*>(ws + delta_bytes(p));
+        dk_acc = dq_acc + qe;
+        dv_acc = dk_acc + (size_t)nsplit * ke;
     }
-    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, qrot, qrot_lo, krot, p->rope_cs,
-                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p)};
+    *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, dk_acc, dv_acc, qrot, qrot_lo, krot, p->rope_cs,
+                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p), nsplit};
     return NE_OK;
 }
 }  // namespace

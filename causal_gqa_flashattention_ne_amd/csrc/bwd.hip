@@ -3,19 +3,23 @@
 //
 // Three launches:
 //   1. bwd_pre:  delta_i = sum_d dO_id * O_id  (float32), and the float32 dQ accumulator zeroed.
-//   2. bwd_main: key/value-tile major.  A workgroup owns BN = 128 keys of one (batch, kv head);
-//      wave w owns keys [32w, 32w + 32).  It walks every query head of the kv group and every
-//      query tile at or after its first key (tiles wholly before the diagonal are skipped) and
-//      recomputes
+//   2. bwd_main: key/value-tile major.  A workgroup owns BN = 128 keys of one (batch, kv head)
+//      and one contiguous share of that tile's steps; wave w owns keys [32w, 32w + 32).  The
+//      steps are every (query head of the kv group, query tile at or after the tile's first key)
+//      (tiles wholly before the diagonal are skipped); a tile's steps are cut into as many shares
+//      as make about a thousand workgroups (one share at long sequences), so that short
+//      sequences still fill the GPU (bwd_f32_splits).  Each step recomputes
 //          S = Q~ K~^T,  P = exp(scale*S - L),  dP = dO V^T,  dS = P * (dP - delta),
 //          dV^T += dO^T P,  dK~^T += Q~^T dS,  dQ~ += dS K~ (float32 atomics, scale applied).
 //      S is formed untransposed here, so one lane owns one key: P and dS are then the B operands
 //      of the dV^T / dK^T products directly from the accumulator registers (the K order of those
 //      products is the accumulator's row order, and Q^T / dO^T are read from LDS in that order).
 //      dS goes through LDS once per step so that all four waves' keys feed the dQ product.
-//      dK and dV of the group are summed over its query heads in registers, so no atomics are
-//      needed for the group sum; dK is un-rotated (R^T) in the epilogue.
-//   3. bwd_dq:   dQ = R^T dQ~ converted to the element type.
+//      dK~ and dV of the share are summed in registers (the group sum over query heads) and
+//      stored into the share's own workspace slice; an empty share stores zeros.
+//   3. bwd_dq:   dQ = R^T dQ~, and dK = R^T (scale sum of the dK~ slices) and dV = sum of the dV
+//      slices, converted to the element type (R^T is linear, so un-rotating the sum equals summing
+//      the un-rotated shares; the slices are added in share order, so dK and dV are deterministic).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -104,11 +108,18 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
 
     const int T_ = a.T;
     const int BG = a.B * a.Hkv;
-    const int jt = (int)(blockIdx.x / BG);       // first blocks own the earliest keys (most work)
-    const int bg = (int)(blockIdx.x % BG);
+    const int nkt = (T_ + kBwdBN - 1) / kBwdBN;
+    const int nsplit = a.nsplit;                 // shares per key tile
+    const int unit = (int)(blockIdx.x % (unsigned)(nkt * BG));
+    const int sp = (int)(blockIdx.x / (unsigned)(nkt * BG));
+    const int jt = unit / BG;                    // first blocks own the earliest keys (most work)
+    const int bg = unit % BG;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.Hq / a.Hkv;
     const int j0 = jt * kBwdBN;
+    const int nq = (T_ - j0 + BM - 1) / BM;      // query tiles at or after the first key
+    const long s_tot = (long)G * nq;
+    const int s_begin = (int)(s_tot * sp / nsplit), s_end = (int)(s_tot * (sp + 1) / nsplit);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -138,12 +149,14 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) { dkt[i] = f32x16{}; dvt[i] = f32x16{}; }
 
-    for (int hh = 0; hh < G; ++hh) {
+    for (int st = s_begin; st < s_end; ++st) {
+        const int hh = st / nq;
+        const int i0 = j0 + (st % nq) * BM;
         const int h = g * G + hh;
         const size_t hrow = (size_t)(b * a.Hq + h) * T_;
         const T* __restrict__ q = reinterpret_cast<const T*>(a.q) + hrow * D;
         const T* __restrict__ dout = reinterpret_cast<const T*>(a.dout) + hrow * D;
-        for (int i0 = j0; i0 < T_; i0 += BM) {
+        {
             __syncthreads();
             // ---- Q~ and dO tiles -> LDS, row-major and transposed; L (log2 units), delta ----
             constexpr int CPR = D / VEC;
@@ -282,21 +295,18 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
         }
     }
 
-    // ---- epilogue: dK = R^T (scale * dK~), dV; lane owns one key, 4 consecutive d per group ----
+    // ---- epilogue: this share's dK~ / scale and dV into its slice (lane owns one key) ----
     if (key < T_) {
-        const size_t base = ((size_t)(b * a.Hkv + g) * T_ + key) * D;
-        T* __restrict__ dk = reinterpret_cast<T*>(a.dk) + base;
-        T* __restrict__ dv = reinterpret_cast<T*>(a.dv) + base;
+        const size_t base = (size_t)sp * a.B * a.Hkv * T_ * D + ((size_t)(b * a.Hkv + g) * T_ + key) * D;
+        float* __restrict__ dka = a.dk_acc + base;
+        float* __restrict__ dva = a.dv_acc + base;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
                 const int d = 32 * dt + acc_row(r, half);
-                float x[4] = {dkt[dt][r] * a.scale, dkt[dt][r + 1] * a.scale, dkt[dt][r + 2] * a.scale,
-                              dkt[dt][r + 3] * a.scale};
-                if (cs) rope_rotate(x, 4, cs, D, key, d, true);
-                store4<T>(dk + d, x[0], x[1], x[2], x[3]);
-                store4<T>(dv + d, dvt[dt][r], dvt[dt][r + 1], dvt[dt][r + 2], dvt[dt][r + 3]);
+                *reinterpret_cast<f32x4*>(dka + d) = f32x4{dkt[dt][r], dkt[dt][r + 1], dkt[dt][r + 2], dkt[dt][r + 3]};
+                *reinterpret_cast<f32x4*>(dva + d) = f32x4{dvt[dt][r], dvt[dt][r + 1], dvt[dt][r + 2], dvt[dt][r + 3]};
             }
     }
 }
@@ -306,7 +316,24 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     const long n4 = (long)a.B * a.Hq * a.T * (D / 4);
     const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= n4) return;
+    if (gid >= n4) {                                   // dK = R^T (scale dK~) and dV
+        const long k4 = gid - n4;
+        if (k4 >= (long)a.B * a.Hkv * a.T * (D / 4)) return;
+        const long row = k4 / (D / 4);
+        const int d0 = (int)(k4 % (D / 4)) * 4;
+        const size_t slice = (size_t)a.B * a.Hkv * a.T * D;
+        f32x4 kv = *reinterpret_cast<const f32x4*>(a.dk_acc + row * D + d0);
+        f32x4 vv = *reinterpret_cast<const f32x4*>(a.dv_acc + row * D + d0);
+        for (int sp = 1; sp < a.nsplit; ++sp) {
+            kv += *reinterpret_cast<const f32x4*>(a.dk_acc + sp * slice + row * D + d0);
+            vv += *reinterpret_cast<const f32x4*>(a.dv_acc + sp * slice + row * D + d0);
+        }
+        float x[4] = {kv[0] * a.scale, kv[1] * a.scale, kv[2] * a.scale, kv[3] * a.scale};
+        if (a.rope_cs) rope_rotate(x, 4, a.rope_cs, D, (int)(row % a.T), d0, true);
+        store4<T>(reinterpret_cast<T*>(a.dk) + row * D + d0, x[0], x[1], x[2], x[3]);
+        store4<T>(reinterpret_cast<T*>(a.dv) + row * D + d0, vv[0], vv[1], vv[2], vv[3]);
+        return;
+    }
     const long row = gid / (D / 4);
     const int d0 = (int)(gid % (D / 4)) * 4;
     const f32x4 v = *reinterpret_cast<const f32x4*>(a.dq_acc + row * D + d0);
@@ -340,14 +367,15 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) attr_set[dev] = true;
     }
-    const long blocks = (long)((a.T + kBwdBN - 1) / kBwdBN) * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), L::BYTES, stream, a);
+    static_assert(kBwdBN == kBwdF32Keys && BwdTile<float>::BM == kBwdF32Queries, "share count assumes these tiles");
+    const long units = (long)((a.T + kBwdBN - 1) / kBwdBN) * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)(units * a.nsplit)), dim3(kThreads), L::BYTES, stream, a);
     return launch_bwd_dq<T, D>(a, stream);
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-    const long threads = (long)a.B * a.Hq * a.T * (D / 4);
+    const long threads = ((long)a.B * a.Hq * a.T + (long)a.B * a.Hkv * a.T) * (D / 4);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();

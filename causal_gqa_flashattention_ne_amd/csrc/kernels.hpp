@@ -33,6 +33,8 @@ struct BwdArgs {
     float* ld;              // workspace (bf16 path): per query head and 64-row tile, 4 groups of
                             // [l' x 16 | delta x 16] (l' = L log2(e) - log2(scale); rows >= T: +inf, 0)
     float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
+    float* dk_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share rotated dK / scale
+    float* dv_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share dV
     void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q rounded to bf16 (hi part)
     void* qrot_lo;          // workspace (bf16 path): [B, Hq, T, D] bf16 remainder, rotated Q = hi + lo
     void* krot;             // workspace (bf16 path): [B, Hkv, T, D] rotated K, written by the preprocess
@@ -40,7 +42,20 @@ struct BwdArgs {
     int B, Hq, Hkv, T;
     int Tp;                 // T rounded up to whole 64-row tiles
     float scale;
+    int nsplit;             // float32 path: shares per key tile (bwd_f32_splits)
 };
+
+// float32 backward: each workgroup owns 128 keys of one (batch, kv head) and one of nsplit
+// contiguous shares of that tile's (query head, 32-query tile) steps.  Enough shares to make
+// about a thousand workgroups at short sequences, at most one step per share, and one share
+// once the key tiles alone are that many.  The workspace holds one dK / dV slice per share.
+constexpr int kBwdF32Keys = 128, kBwdF32Queries = 32;
+inline int bwd_f32_splits(int B, int Hq, int Hkv, int T) {
+    const long units = (long)((T + kBwdF32Keys - 1) / kBwdF32Keys) * B * Hkv;
+    const long steps = (long)(Hq / Hkv) * ((T + kBwdF32Queries - 1) / kBwdF32Queries);
+    const long want = (1024 + units - 1) / units;
+    return (int)(want < 1 ? 1 : (want < steps ? want : steps));
+}
 
 struct DecodeArgs {
     const void* q;          // [B, Hq, n, D] new tokens, un-rotated

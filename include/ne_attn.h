@@ -113,8 +113,8 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace that ne_attn_bwd needs for these parameters (0 on a bad shape): float32,
- * delta and a float32 dQ accumulator; bf16, the per-row exponent offsets and deltas, the rotated
- * queries (two bf16 parts) and the rotated keys. */
+ * delta and float32 dQ, dK and dV accumulators; bf16, the per-row exponent offsets and deltas, the
+ * rotated queries (two bf16 parts) and the rotated keys. */
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);
 
 /*
@@ -137,7 +137,7 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
  *
  * ne_attn_bwd_preprocess: delta_i = sum_d dout_id * o_id (float32) for every query row, the
  * per-row term of the softmax backward dS = P * (dP - delta), written into the workspace, which
- * it also prepares for ne_attn_bwd_main (float32: a zeroed dQ accumulator; bf16: the rotated
+ * it also prepares for ne_attn_bwd_main (float32: zeroed dQ, dK and dV accumulators; bf16: the rotated
  * queries R q and keys R k and, from lse, the per-row exponent offset).  Reads q, k, o, lse and
  * dout; writes only the workspace.
  *
