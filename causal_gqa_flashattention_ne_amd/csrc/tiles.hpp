@@ -97,10 +97,14 @@ __device__ inline void wait_vmcnt() {
 }
 
 // Barrier between the waves of the workgroup without a memory fence (the fence of
-// __syncthreads would also wait for the copies still in flight); the empty asm keeps the
-// compiler from moving LDS accesses across it.
+// __syncthreads would also wait for the copies still in flight).  The empty asm keeps the
+// compiler from moving LDS accesses across it, and the lgkmcnt(0) wait before it makes every LDS
+// read this wave issued complete before any wave passes: the stage those reads came from is
+// refilled by copies issued right after the barrier, and the compiler may otherwise place a
+// read's consumer, and so the wait for it, after the barrier (vmcnt and expcnt not waited for).
 __device__ inline void step_barrier() {
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
