@@ -7,6 +7,9 @@
         --pmc WRITE_SIZE) of `bench.py --copy-calibration`, each scaled by what the same counter
         reads for the calibration copy (256 MiB read + 256 MiB written per launch), tagged with a
         hash of each kernel's sources so that the benchmark stops quoting it once that kernel changes.
+    python -m causal_gqa_flashattention_ne_amd.profsum last <N> <kernel_trace.csv>
+        per-kernel average duration over each kernel's last N dispatches (for bench.py, whose last
+        K dispatches of each call are that call's back-to-back launches).
     python -m causal_gqa_flashattention_ne_amd.profsum counters <dir> [<dir> ...]
         per-kernel averages over dispatches of every counter or derived metric in the
         counter_collection.csv files of one or more --pmc runs (e.g. MfmaUtil, MfmaFlopsBF16,
@@ -96,6 +99,18 @@ def counters(dirs):
                                             for c in names))
 
 
+def last_n(n, path):
+    per = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    print("%-64s %6s %10s" % ("kernel", "last_n", "avg_us"))
+    for name, v in sorted(per.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        v.sort()
+        tail = v[-n:]
+        print("%-64s %6d %10.2f" % (name[:64], len(tail), sum(e - s for s, e in tail) / len(tail) / 1e3))
+
+
 def rows_from_db(path):
     c = sqlite3.connect(path)
     q = ("select name, count(*), avg(end-start)/1000.0, min(end-start)/1000.0, max(end-start)/1000.0, "
@@ -122,6 +137,8 @@ def main(path):
 if __name__ == "__main__":
     if sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "last":
+        last_n(int(sys.argv[2]), sys.argv[3])
     elif sys.argv[1] == "counters":
         counters(sys.argv[2:])
     else:
