@@ -1,6 +1,7 @@
 """GPU properties that hold at any size: standalone RoPE vs the oracle, the RoPE table, bitwise
-forward determinism, causal invariance of the forward, GQA = MHA with repeated K/V, and the
-sum_t R_t dK_t = 0 identity at full size.
+forward determinism, bitwise determinism of the bf16 backward (no atomics) and of the float32 dK
+and dV (per-share slices summed in order), causal invariance of the forward, GQA = MHA with
+repeated K/V, and the sum_t R_t dK_t = 0 identity at full size.
 """
 import numpy as np
 import pytest
@@ -56,6 +57,33 @@ def test_forward_bitwise_deterministic_and_causal_invariant(dtype):
     assert np.array_equal(a[1][:, :, :i0 + 1], c[1][:, :, :i0 + 1])
     # dQ of earlier rows depends only on earlier positions (float32 atomics: compare to tolerance)
     assert rel_err(c[2][:, :, :i0 + 1], a[2][:, :, :i0 + 1]) <= TOL[dtype] / 10
+
+
+@pytest.mark.parametrize("shape", [(2, 6, 2, 300, 64), "gpt116m-layer-bf16"])
+def test_backward_bitwise_deterministic_bf16(shape):
+    # the bf16 backward sums with no atomics (dK/dV over the group's heads in registers, dQ once
+    # per query block), so two runs on the same inputs agree bit for bit, also on the full layer
+    if isinstance(shape, str):
+        w = next(x for x in gen.WORKLOADS.values() if x.name == shape)
+        q, k, v, do = gen.layer_inputs(w)
+    else:
+        B, Hq, Hkv, T, D = shape
+        q, k, v, do = gen.small_case(71, B, Hq, Hkv, T, D, "bf16")
+    a = run_gpu(q, k, v, do, "bf16")
+    b = run_gpu(q, k, v, do, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_dk_dv_bitwise_deterministic_f32():
+    # float32: dQ goes through atomics (bits may vary), dK and dV through per-share slices that the
+    # finalize pass adds in share order (bits may not)
+    q, k, v, do = gen.small_case(72, 2, 4, 2, 200, 32, "f32")
+    a = run_gpu(q, k, v, do, "f32")
+    b = run_gpu(q, k, v, do, "f32")
+    for i in (0, 1, 3, 4):
+        assert np.array_equal(a[i], b[i])
+    assert rel_err(a[2], b[2]) <= 1e-6
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
