@@ -463,8 +463,13 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     }
 }
 
+// workgroups per CU the kernel is compiled for: two (≤ 256 registers per wave) up to head_dim 64;
+// at 128 a dK/dV wave needs more than 256, so one
+template <int D> struct BwdOcc { static constexpr int MINB = 2; };
+template <> struct BwdOcc<128> { static constexpr int MINB = 1; };
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, BwdOcc<D>::MINB) void bwd_bf16_kernel(BwdArgs a) {
     __shared__ BwdLds<D> S;
     const int BG = a.B * a.Hkv, G = a.Hq / a.Hkv;
     const int nkv = (a.T + kTile - 1) / kTile;

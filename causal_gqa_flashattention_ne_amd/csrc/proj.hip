@@ -216,7 +216,6 @@ __global__ __launch_bounds__(kBlockThreads, 2) void proj_kernel(ProjArgs a) {
     __syncthreads();
     // 16-byte runs: 8 features of one token, inside one head (D is a multiple of 8)
     constexpr int kRuns = kTok * kFeat / 8;
-#pragma unroll
     for (int i = threadIdx.x; i < kRuns; i += kBlockThreads) {
         const int tok = i / (kFeat / 8), f8 = (i % (kFeat / 8)) * 8;
         const int m = m0 + tok, n = n0 + f8;
