@@ -381,14 +381,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template hipError_t launch_bwd_dq<bf16, 64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_dq<bf16, 32>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<float, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<float, 32>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_pre<bf16, 64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_main<bf16, 64>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_pre<bf16, 32>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd_main<bf16, 32>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre<float, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_main<float, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_pre<float, 32>(const BwdArgs&, hipStream_t);

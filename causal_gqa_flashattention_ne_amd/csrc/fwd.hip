@@ -208,8 +208,6 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, hipStream_t);
-template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const FwdArgs&, hipStream_t);
 
