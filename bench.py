@@ -54,11 +54,38 @@ def parse():
     ap.add_argument("--qkv", type=int, default=0, help="projection workload id (1) instead of the training step")
     ap.add_argument("--block", type=int, default=0, help="1: attention block forward + backward instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cores))")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (default: the host cores this process may use, see host_threads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the bench, run a plain 256 MiB elementwise copy 5 times (reference kernel of "
                          "known traffic for HBM byte counters)")
     return ap.parse_args()
+
+
+def host_threads():
+    """Host cores the oracle may use: OMP_NUM_THREADS when the environment sets it (a GPU machine gives
+    each GPU a fixed share of its cores this way), else every core of this process's affinity."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def host_info():
+    """Total logical cores of the host and its CPU model (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cores": os.cpu_count(), "cpu_model": model}
 
 
 def kernel_bytes(w, elem):
@@ -236,7 +263,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or host_threads()
         q, k, v, do = host_inputs
         groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
         # bounded sample: whole kv groups of layer 0, up to ~10-30 s of CPU work
@@ -253,6 +280,14 @@ def main():
                "sample": "%d of %d (batch, kv group) units of layer 0 (all %d query heads each, all T=%d "
                          "positions), forward+backward in double, %.2f s wall" %
                          (len(sample), len(groups), w.G, w.T, dt)}
+        cpu.update(host_info())
+        if w.dtype == "f32":
+            # the small float32 workloads: the same sample on one core as well
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, do, theta=w.theta, groups=sample, nthreads=1)
+            dt1 = time.perf_counter() - t0
+            cpu["single_thread"] = {"value": sample_flop / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                    "seconds": dt1}
 
     out = {
         "metric": METRIC,
@@ -348,7 +383,7 @@ def bench_qkv(args, dev):
     if not args.no_cpu_baseline:
         import oracle
         from threadpoolctl import threadpool_limits
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or host_threads()
         with threadpool_limits(limits=threads):
             t_s = time.perf_counter()
             passes = 0
@@ -361,6 +396,7 @@ def bench_qkv(args, dev):
         cpu = {"value": flop * passes / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                "sample": "the whole projection in double (numpy matmul + RoPE) x %d passes, %.2f s wall"
                          % (passes, dt)}
+        cpu.update(host_info())
 
     out = {
         "metric": "query/key/value projection with RoPE epilogue, TFLOP/s",
@@ -443,7 +479,7 @@ def bench_block(args, dev):
     if not args.no_cpu_baseline:
         import oracle
         from threadpoolctl import threadpool_limits
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or host_threads()
         xs, ws, gs, wos, dys = x[:1], wqkv, g.float().cpu().numpy(), wo.float().cpu().numpy(), dy[:1].float().cpu().numpy()
         flop1 = flop / B                                 # one sequence
         with threadpool_limits(limits=threads):
@@ -458,6 +494,7 @@ def bench_block(args, dev):
         out["cpu_baseline"] = {"value": flop1 * passes / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
                                "kind": "oracle", "sample": "1 of %d sequences x %d passes, block forward + "
                                "backward in double, %.2f s wall" % (B, passes, dt)}
+        out["cpu_baseline"].update(host_info())
     print(json.dumps(out))
 
 
@@ -539,6 +576,7 @@ def bench_decode(args, dev):
         cpu = {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": "%d of %d sequences x %d passes, decode in double over the oracle-rotated cache, "
                          "%.2f s wall" % (done, w.B, passes, dt)}
+        cpu.update(host_info())
 
     out = {
         "metric": "decode attention, algorithmic HBM GB/s of one call (KV cache read once)",

@@ -132,11 +132,19 @@ __device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(l
 // tiles two steps ahead.  Every wait on them is the explicit wait_vmcnt at the top of a step; the
 // per-lane operands a kernel loads before its step loop are waited for (vmcnt(0)) before the loop
 // starts, so no other vector-memory load is in flight in it.
+//
+// Wait states.  soff and the descriptor are scalar registers that a VALU instruction
+// (v_readfirstlane) may have written just before this block, and the gfx9 family (gfx950
+// included) requires 5 wait states between a VALU write of an SGPR and a vector-memory
+// instruction that reads it; M0 written by a scalar move needs 1 before an LDS-direct load.  The
+// compiler inserts these waits for the loads it emits itself but cannot see inside this
+// assembly, so the block opens with s_nop 4 (5 wait states), which covers both whatever the
+// compiler placed in front of it.
 __device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
     // soff and lds are wave-uniform; readfirstlane puts them in scalar registers even where the
     // compiler kept a uniform value in a vector register
     const unsigned so = __builtin_amdgcn_readfirstlane(soff), m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(so), "{m0}"(m0)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(so), "{m0}"(m0)
                  : "memory");
 }
 

@@ -53,3 +53,42 @@ def test_train_pair_workload_full_size(cfg):
     log("train pair workload %s" % w.name)
     q, k, v, do = gen.layer_inputs(w, 0)
     check(q, k, v, do, w.dtype, theta=w.theta, label=w.name + " (training pair)", train=True)
+
+
+def test_train_pair_every_layer_of_the_stack():
+    """The 16-layer stack as the benchmark runs it: every layer's inputs resident at once, one
+    workspace shared by all layers, and one step (training forward, preprocess, backward main per
+    layer, in layer order) before any output is read; then every layer's whole output tensors
+    against the oracle."""
+    import torch
+
+    import causal_gqa_flashattention_ne_amd as ne
+    import oracle
+    from parity_util import TOL, compare, to_dev, to_np
+
+    w = gen.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    cs = ne.rope_table(w.T, w.D, w.theta, dev)
+    p = ne.make_params(w.B, w.Hq, w.Hkv, w.T, w.D, ne.NE_DTYPE_BF16, None, cs)
+    ws = torch.full((ne.bwd_workspace_bytes(p),), 0xFF, dtype=torch.uint8, device=dev)
+    host, dev_in, outs = [], [], []
+    for layer in range(w.layers):
+        q, k, v, do = gen.layer_inputs(w, layer)
+        host.append((q, k, v, do))
+        dev_in.append(tuple(to_dev(x, w.dtype) for x in (q, k, v, do)))
+        qd, kd = dev_in[-1][0], dev_in[-1][1]
+        outs.append((torch.full_like(qd, float("nan")),
+                     torch.full((w.B, w.Hq, w.T), float("nan"), dtype=torch.float32, device=dev),
+                     torch.full_like(qd, float("nan")), torch.full_like(kd, float("nan")),
+                     torch.full_like(kd, float("nan"))))
+    for (qd, kd, vd, dod), (o, lse, dq, dk, dv) in zip(dev_in, outs):
+        ne.attn_fwd_train_into(p, qd, kd, vd, o, lse, ws)
+        ne.attn_bwd_train_preprocess_into(p, qd, kd, o, lse, dod, ws)
+        ne.attn_bwd_main_into(p, qd, kd, vd, lse, dod, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for layer, ((q, k, v, do), t) in enumerate(zip(host, outs)):
+        ref = oracle.attention(q, k, v, do, theta=w.theta)
+        errs = compare(tuple(to_np(x) for x in t), ref, w.dtype)
+        log("stack layer %d errors %s" % (layer, errs))
+        bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
+        assert not bad, "layer %d: %s" % (layer, errs)
