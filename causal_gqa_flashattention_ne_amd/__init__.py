@@ -27,12 +27,13 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
            "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main",
            "ne_attn_decode_workspace_bytes", "ne_attn_decode", "ne_qkv_proj", "ne_attn_fwd_train",
-           "ne_attn_bwd_train", "ne_attn_bwd_train_preprocess")
+           "ne_attn_bwd_train", "ne_attn_bwd_train_preprocess", "ne_attn_decode_static",
+           "ne_attn_decode_static_max_bytes")
 
 
 class AttnParams(ctypes.Structure):
@@ -95,13 +96,16 @@ def lib():
         L.ne_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
         L.ne_attn_decode_workspace_bytes.restype = sz
         L.ne_attn_decode.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 7 + [sz, vp]
+        L.ne_attn_decode_static.argtypes = [ctypes.POINTER(DecodeParams)] + [vp] * 6 + [vp]
+        L.ne_attn_decode_static_max_bytes.argtypes = []
+        L.ne_attn_decode_static_max_bytes.restype = sz
         L.ne_qkv_proj.argtypes = [ctypes.POINTER(QkvParams)] + [vp] * 6
         L.ne_attn_fwd_train.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         L.ne_attn_bwd_train.argtypes = [ctypes.POINTER(AttnParams)] + [vp] * 9 + [vp, sz, vp]
         L.ne_attn_bwd_train_preprocess.argtypes = [ctypes.POINTER(AttnParams), vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("ne_rope_table", "ne_rope_apply", "ne_attn_fwd", "ne_attn_bwd", "ne_attn_bwd_preprocess",
-                  "ne_attn_bwd_main", "ne_attn_decode", "ne_qkv_proj", "ne_attn_fwd_train", "ne_attn_bwd_train",
-                  "ne_attn_bwd_train_preprocess"):
+                  "ne_attn_bwd_main", "ne_attn_decode", "ne_attn_decode_static", "ne_qkv_proj", "ne_attn_fwd_train",
+                  "ne_attn_bwd_train", "ne_attn_bwd_train_preprocess"):
             getattr(L, f).restype = ctypes.c_int
         if L.ne_abi_version() != ABI_VERSION:
             raise ImportError("libne_attn.so ABI %d, binding expects %d" % (L.ne_abi_version(), ABI_VERSION))
@@ -300,6 +304,19 @@ def attn_decode_into(p: DecodeParams, q, k_cache, v_cache, kv_len, o, lse, ws, s
     st = stream if stream is not None else _stream(q.device)
     _check("ne_attn_decode", lib().ne_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
                                                   _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), st))
+
+
+def attn_decode_static_into(p: DecodeParams, q, k_cache, v_cache, kv_len, o, lse, stream=None):
+    """Decode into preallocated o / lse with no workspace: the partial results live in the library's
+    own per-device array (ne_attn_decode_static).  Calls on one GPU must not overlap in time."""
+    st = stream if stream is not None else _stream(q.device)
+    _check("ne_attn_decode_static", lib().ne_attn_decode_static(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                                _ptr(kv_len), _ptr(o), _ptr(lse), st))
+
+
+def decode_static_max_bytes() -> int:
+    """Size of the library's per-device array behind ne_attn_decode_static."""
+    return int(lib().ne_attn_decode_static_max_bytes())
 
 
 def attn_decode(q, k_cache, v_cache, kv_len, rope_theta: float = 10000.0, scale=None):

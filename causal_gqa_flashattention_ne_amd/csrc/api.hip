@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/ne_attn.h"
@@ -149,6 +150,99 @@ int check_decode(const ne_decode_params* p) {
     return NE_OK;
 }
 
+// Where the decode kernels keep their partial results.  16-column path: arrival counters (zero
+// between calls), piece L and piece O for up to max_waves waves plus one slot per segment.
+// 32-column path: chunk O then chunk L from part32.
+struct DecodeSpace {
+    char* ctr;
+    char* part32_or_l;   // 32-column path: chunk outputs; 16-column path: piece L
+    char* part_o;        // 16-column path: piece O
+    long max_waves;      // 16-column path: cap on the grid's waves (the pieces' slots)
+};
+
+int decode_launch(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* kv_len, void* o, float* lse, const DecodeSpace& sp, hipStream_t s) {
+    const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
+    hipError_t e;
+    if (decode_narrow(p)) {
+        const Decode16Layout L(p);
+        const int slots = p->D == 128 ? ne::decode16_slots<128>()
+                          : p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
+        if (slots <= 0) return NE_ERR_HIP;
+        const long waves = decode16_waves(p, L, (int)std::min<long>(slots, sp.max_waves));
+        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse,
+                         reinterpret_cast<float*>(sp.part_o), reinterpret_cast<float*>(sp.part32_or_l),
+                         reinterpret_cast<int*>(sp.ctr), p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows,
+                         (int)std::max<long>(1, waves), 0, scale};
+        e = p->D == 128 ? ne::launch_decode16<128>(a, s)
+            : p->D == 64 ? ne::launch_decode16<64>(a, s) : ne::launch_decode16<32>(a, s);
+    } else {
+        int nsplit, chunk;
+        decode_split(p, &nsplit, &chunk);
+        const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse, reinterpret_cast<float*>(sp.part32_or_l),
+                         reinterpret_cast<float*>(sp.part32_or_l + align256(parts * p->D * sizeof(float))), nullptr,
+                         p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows, nsplit, chunk, scale};
+        e = p->D == 64 ? ne::launch_decode<64>(a, s) : ne::launch_decode<32>(a, s);
+    }
+    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+}
+
+// ---- the allocation-free decode: partial results in a library-owned device array ----
+//
+// One array per device, in the library's code object (each GPU holds its own copy until the
+// process ends).  Layout: arrival counters of the 16-column path in the first kStaticCtrBytes
+// (zeroed once per device at set-up; every call leaves them at zero again), then the pieces of
+// either path.  Calls on one GPU share it: calls that overlap in time on one GPU race.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr size_t kStaticCtrBytes = (size_t)64 << 10;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ void zero_words_kernel(unsigned* p, unsigned n) {
+    const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxStaticDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxStaticDevices];
+
+// The device address of this device's array (hipGetSymbolAddress with that device current; the
+// name `scratch` itself is a host-side stand-in, never passed to a kernel), its counters zeroed
+// on the first use on a device (a fill kernel on the caller's stream).
+int static_scratch(hipStream_t s, char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxStaticDevices) return NE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return NE_ERR_HIP;
+        const unsigned words = (unsigned)(kStaticCtrBytes / 4);
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s, static_cast<unsigned*>(ptr), words);
+        if (hipGetLastError() != hipSuccess) return NE_ERR_HIP;
+        g_static_ptr[dev] = ptr;
+    }
+    *out = static_cast<char*>(g_static_ptr[dev]);
+    return NE_OK;
+}
+
+// Most waves whose pieces fit in the static array after the counters (16-column path), or -1 when
+// not even one wave's do; bytes needed by the 32-column path.
+long static_decode16_waves(const ne_decode_params* p) {
+    const long nseg = (long)p->B * p->Hkv;
+    if (nseg * (long)sizeof(int) > (long)kStaticCtrBytes) return -1;
+    const size_t room = kStaticScratchBytes - kStaticCtrBytes;
+    const size_t per_slot = 16 * sizeof(float) + 16 * (size_t)p->D * sizeof(float);
+    const long slots = (long)((room - 256) / per_slot);      // align256 of the L part costs < 256 bytes
+    return slots - nseg >= 1 ? slots - nseg : -1;
+}
+size_t static_decode32_bytes(const ne_decode_params* p) {
+    int nsplit, chunk;
+    decode_split(p, &nsplit, &chunk);
+    const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
+    return align256(parts * p->D * sizeof(float)) + parts * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,32 +337,15 @@ int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache
     if (int rc = check_decode(p)) return rc;
     if (int rc = check_ptrs({q, k_cache, v_cache, kv_len, o, lse, workspace})) return rc;
     if (workspace_bytes < ne_attn_decode_workspace_bytes(p)) return NE_ERR_WORKSPACE;
-    const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
     char* ws = static_cast<char*>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    DecodeSpace sp;
     if (decode_narrow(p)) {
         const Decode16Layout L(p);
-        const int slots = p->D == 128 ? ne::decode16_slots<128>()
-                          : p->D == 64 ? ne::decode16_slots<64>() : ne::decode16_slots<32>();
-        if (slots <= 0) return NE_ERR_HIP;
-        const long waves = decode16_waves(p, L, slots);
-        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse,
-                         reinterpret_cast<float*>(ws + L.part_o), reinterpret_cast<float*>(ws + L.part_l),
-                         reinterpret_cast<int*>(ws + L.ctr), p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows,
-                         (int)std::max<long>(1, waves), 0, scale};
-        e = p->D == 128 ? ne::launch_decode16<128>(a, s)
-            : p->D == 64 ? ne::launch_decode16<64>(a, s) : ne::launch_decode16<32>(a, s);
+        sp = DecodeSpace{ws + L.ctr, ws + L.part_l, ws + L.part_o, L.wcap};
     } else {
-        int nsplit, chunk;
-        decode_split(p, &nsplit, &chunk);
-        const size_t parts = (size_t)p->B * p->Hkv * nsplit * 32;
-        ne::DecodeArgs a{q, k_cache, v_cache, kv_len, o, lse, reinterpret_cast<float*>(ws),
-                         reinterpret_cast<float*>(ws + align256(parts * p->D * sizeof(float))), nullptr,
-                         p->rope_cs, p->B, p->Hq, p->Hkv, p->n, p->cache_rows, nsplit, chunk, scale};
-        e = p->D == 64 ? ne::launch_decode<64>(a, s) : ne::launch_decode<32>(a, s);
+        sp = DecodeSpace{nullptr, ws, nullptr, 0};
     }
-    return e == hipSuccess ? NE_OK : NE_ERR_HIP;
+    return decode_launch(p, q, k_cache, v_cache, kv_len, o, lse, sp, static_cast<hipStream_t>(stream));
 }
 
 int ne_qkv_proj(const ne_qkv_params* p, const void* x, const void* w, void* q, void* k, void* v, void* stream) {
@@ -443,6 +520,30 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
     if (workspace_bytes < ne_attn_bwd_workspace_bytes(p)) return NE_ERR_WORKSPACE;
     if (int rc = ne_attn_bwd_preprocess(p, q, k, o, lse, dout, workspace, workspace_bytes, stream)) return rc;
     return ne_attn_bwd_main(p, q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+size_t ne_attn_decode_static_max_bytes(void) { return kStaticScratchBytes; }
+
+int ne_attn_decode_static(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_len, void* o, float* lse, void* stream) {
+    if (int rc = check_decode(p)) return rc;
+    if (int rc = check_ptrs({q, k_cache, v_cache, kv_len, o, lse})) return rc;
+    const bool narrow = decode_narrow(p);
+    const long wmax = narrow ? static_decode16_waves(p) : 0;
+    if (narrow ? wmax < 1 : static_decode32_bytes(p) > kStaticScratchBytes - kStaticCtrBytes)
+        return NE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = nullptr;
+    if (int rc = static_scratch(s, &base)) return rc;
+    DecodeSpace sp;
+    if (narrow) {
+        const long slots = wmax + (long)p->B * p->Hkv;
+        char* pl = base + kStaticCtrBytes;
+        sp = DecodeSpace{base, pl, pl + align256((size_t)slots * 16 * sizeof(float)), wmax};
+    } else {
+        sp = DecodeSpace{nullptr, base + kStaticCtrBytes, nullptr, 0};
+    }
+    return decode_launch(p, q, k_cache, v_cache, kv_len, o, lse, sp, s);
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 6
+#define NE_ABI_VERSION 7
 
 enum {
     NE_OK = 0,
@@ -214,6 +214,25 @@ size_t ne_attn_decode_workspace_bytes(const ne_decode_params* p);
 int ne_attn_decode(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* kv_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * ne_attn_decode without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same operation,
+ * arguments and results as ne_attn_decode, with the partial results kept in a device array that
+ * the library itself holds (one per GPU, in the library's code object, until the process ends;
+ * ne_attn_decode_static_max_bytes() bytes, 32 MiB).  The call allocates nothing.
+ *   Its first call on a device zeroes the array's arrival counters with a small kernel on stream;
+ *   every call leaves them at zero again.  All calls on one GPU share the array: calls that
+ *   overlap in time on one GPU (same or different streams, host threads) race and must not.
+ *   The 16-column path may run fewer waves than ne_attn_decode would (as many as the array holds
+ *   the pieces of), so results agree with ne_attn_decode to rounding, not always bit for bit.
+ * Returns NE_ERR_WORKSPACE, before any launch, when the partial results of this shape do not fit
+ * (more than 16384 (sequence, kv head) pairs, or not even one wave's pieces); other errors as for
+ * ne_attn_decode.
+ */
+size_t ne_attn_decode_static_max_bytes(void);
+int ne_attn_decode_static(const ne_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_len, void* o, float* lse, void* stream);
 
 /*
  * The query, key and value projections of an attention block, with RoPE on the queries and keys,
