@@ -56,6 +56,15 @@ size_t delta_bytes(const ne_attn_params* p) {
     return (n + 255) & ~(size_t)255;
 }
 
+// bf16: max |k| per 64-row key tile [B, Hkv, ceil(T/64)] and low-part flags per 128-row query
+// block [B, Hq, ceil(T/128)]
+size_t key_bound_bytes(const ne_attn_params* p) {
+    return ((size_t)p->B * p->Hkv * ((p->T + 63) / 64) * sizeof(float) + 255) & ~(size_t)255;
+}
+size_t lo_flag_bytes(const ne_attn_params* p) {
+    return ((size_t)p->B * p->Hq * ((p->T + 127) / 128) * sizeof(int) + 255) & ~(size_t)255;
+}
+
 // the attention kernels: bf16 with D in {32, 64, 128}, fp32 with D in {32, 64}
 template <typename F>
 int dispatch(int dtype, int D, F&& f) {
@@ -288,9 +297,10 @@ int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, 
 
 size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
-    // bf16 with RoPE: the rotated keys, written once and read by every query head of their group
-    if (p->dtype == NE_DTYPE_BF16 && p->rope_cs) return (size_t)p->B * p->Hkv * p->T * p->D * 2;
-    return 0;
+    if (p->dtype != NE_DTYPE_BF16) return 0;
+    // bf16: max |k| per 64-row key tile, then (with RoPE) the rotated keys, written once and read by
+    // every query head of their group
+    return key_bound_bytes(p) + (p->rope_cs ? (size_t)p->B * p->Hkv * p->T * p->D * 2 : 0);
 }
 
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
@@ -309,12 +319,13 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
         if constexpr (std::is_same<T, ne::bf16>::value) {
-            if (need) {
-                ne::RopeArgs r{k, workspace, p->rope_cs, p->B * p->Hkv * p->T, p->T, 0, 0};
-                const hipError_t e = ne::launch_rope<T, DD>(r, s);
-                if (e != hipSuccess) return e;
-                a.k = workspace;
-            }
+            char* ws = static_cast<char*>(workspace);
+            float* ak = reinterpret_cast<float*>(ws);
+            void* krot = p->rope_cs ? ws + key_bound_bytes(p) : nullptr;
+            const hipError_t e = ne::launch_key_rot<DD>(ne::KeyRotArgs{k, krot, ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
+            if (e != hipSuccess) return e;
+            if (krot) a.k = krot;
+            a.ak = ak;
             return ne::launch_fwd_bf16<DD>(a, s);
         } else {
             return ne::launch_fwd<T, DD>(a, s);
@@ -374,8 +385,10 @@ size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
     // float32: delta | float32 dQ accumulator | dK and dV slices, one per share of a key tile
-    // bf16: (l', delta) per row | rotated Q hi | rotated Q lo | rotated K
-    if (p->dtype == NE_DTYPE_BF16) return delta_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
+    // bf16: (-l', -delta) per row | low-part flags | max |k| per key tile | scaled rotated Q hi | lo |
+    // rotated K
+    if (p->dtype == NE_DTYPE_BF16)
+        return delta_bytes(p) + lo_flag_bytes(p) + key_bound_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
     const size_t ns = (size_t)ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
     return delta_bytes(p) + (qe + 2 * ns * ke) * sizeof(float);
 }
@@ -396,13 +409,22 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
     void* qrot = nullptr;
     void* qrot_lo = nullptr;
     void* krot = nullptr;
+    int* lof = nullptr;
+    float* ak = nullptr;
     int nsplit = 1;
     if (p->dtype == NE_DTYPE_BF16) {
         const size_t qb = (qe * 2 + 255) & ~(size_t)255;
-        ld = reinterpret_cast<float*>(ws);
-        qrot = ws + delta_bytes(p);
-        qrot_lo = ws + delta_bytes(p) + qb;
-        krot = ws + delta_bytes(p) + 2 * qb;
+        char* x = ws;
+        ld = reinterpret_cast<float*>(x);
+        x += delta_bytes(p);
+        lof = reinterpret_cast<int*>(x);
+        x += lo_flag_bytes(p);
+        ak = reinterpret_cast<float*>(x);
+        x += key_bound_bytes(p);
+        qrot = x;
+        qrot_lo = x + qb;
+        // without RoPE the kernels read the keys themselves
+        krot = p->rope_cs ? x + 2 * qb : const_cast<void*>(k);
     } else {
         delta = reinterpret_cast<float*>(ws);
         const size_t ke = (size_t)p->B * p->Hkv * p->T * p->D;
@@ -412,7 +434,7 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
         dv_acc = dk_acc + (size_t)nsplit * ke;
     }
     *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, dk_acc, dv_acc, qrot, qrot_lo, krot, p->rope_cs,
-                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p), nsplit};
+                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p), nsplit, lof, ak};
     return NE_OK;
 }
 }  // namespace
@@ -429,8 +451,14 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
-        if constexpr (std::is_same<T, ne::bf16>::value) return ne::launch_bwd_pre_bf16<DD>(a, s);
-        else return ne::launch_bwd_pre<T, DD>(a, s);
+        if constexpr (std::is_same<T, ne::bf16>::value) {
+            const hipError_t e = ne::launch_key_rot<DD>(
+                ne::KeyRotArgs{k, p->rope_cs ? a.krot : nullptr, a.ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
+            if (e != hipSuccess) return e;
+            return ne::launch_bwd_pre_bf16<DD>(a, s);
+        } else {
+            return ne::launch_bwd_pre<T, DD>(a, s);
+        }
     });
 }
 
@@ -443,19 +471,16 @@ int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, con
     if (int rc = bwd_args(p, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, &b))
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    ne::FwdArgs a{q, b.krot, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p), b.qrot, b.qrot_lo};
+    ne::FwdArgs a{q, b.krot, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p), b.qrot, b.qrot_lo,
+                  b.ak, b.lof};
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
         if constexpr (std::is_same<T, ne::bf16>::value) {
-            // the keys as the backward reads them: rotated once here, or copied when there is no RoPE
-            hipError_t e;
-            if (p->rope_cs) {
-                ne::RopeArgs r{k, b.krot, p->rope_cs, p->B * p->Hkv * p->T, p->T, 0, 0};
-                e = ne::launch_rope<T, DD>(r, s);
-            } else {
-                e = hipMemcpyAsync(b.krot, k, (size_t)p->B * p->Hkv * p->T * DD * sizeof(T), hipMemcpyDeviceToDevice, s);
-            }
+            // the keys as the backward reads them (rotated once here; without RoPE the raw keys)
+            // and their tile bounds
+            const hipError_t e = ne::launch_key_rot<DD>(
+                ne::KeyRotArgs{k, p->rope_cs ? b.krot : nullptr, b.ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
             if (e != hipSuccess) return e;
             return ne::launch_fwd_bf16<DD>(a, s);
         } else {

@@ -6,16 +6,21 @@
 //     dV = P^T dO,  dK = R^T (scale * dS^T Q~),  dQ = R^T (scale * dS K~),
 // where delta_i = sum_d dO_id O_id.  The kernels work with P' = scale * P and dS' = scale * dS:
 // the factor enters through the exponent (l' = L log2(e) - log2(scale) is what the kernels
-// subtract), so dS' feeds dK and dQ directly and dV is divided by scale once at the end.
+// subtract), so dS' feeds dK and dQ directly and dV is divided by scale once at the end.  The
+// rotated queries are stored multiplied by c = scale * log2(e), Q~' = c Q~, so that Q~' K~^T is
+// the score in log2 units; dK, formed from Q~', is divided by c once at the end.
 //
-// The rotated queries are carried as two bf16 parts, Q~ = hi + lo, in every score product (the
-// forward does the same): S then carries only the rounding of the rotated keys, which keeps the
-// byte-level workload (keys scaled x8) inside the bf16 error bar; Q~^T in the dK product uses hi.
+// The rotated queries are rounded to bf16 (hi).  For the 128-query blocks whose score bound
+// exceeds kLoBound the forward also keeps the remainder (lo) and adds its products to every score
+// of the block, so that S carries only the rounding of the rotated keys there (this keeps the
+// byte-level workload, keys scaled x8, inside the bf16 error bar); the backward follows the
+// forward's per-block flags (lof), so that P is formed from the same products in both.  Q~'^T in
+// the dK product uses hi.
 //
-// Two launches:
-//   bwd_pre_bf16:  per query row delta and l' (float32, padded per head to whole 64-row tiles:
-//     +inf / 0 past the sequence end, so padded rows get P = 0), Q~ (hi and lo) and K~ (bf16,
-//     rotated once), all into the workspace.
+// Launches:
+//   bwd_pre_bf16:  per query row -l' and -delta (float32, padded per head to whole 64-row tiles:
+//     -inf / 0 past the sequence end, so padded rows get P = 0); in the plain backward also Q~'
+//     (hi, and lo for the flagged blocks) and the flags.  K~ comes from key_rot_kernel.
 //   bwd_bf16:      one grid, two kinds of workgroups, no atomics and no float32 scratch:
 //     dK/dV blocks (key-tile major): a block owns 64 keys of one (batch, kv head); its 4 waves
 //       split every 64-query step 2 x 2 (wave w: keys 32*(w&1).., queries 32*(w>>1)..), keep
@@ -28,6 +33,8 @@
 //       queries 32w..32w+31, one lane per query.  Key/value tiles of 64 stream through LDS;
 //       S^T = K~ Q~^T and dP^T = V dO^T put one query per lane, and dQ^T += K~^T dS'^T takes
 //       dS'^T straight from the registers.  dQ is un-rotated and written once.
+//   The l' and delta of a step's rows are the starting values of its S and dP accumulators in the
+//   dK/dV role (stored negated), so the products themselves subtract them.
 //   Tiles reach LDS through the copy pipeline of tiles.hpp with two stages (buffer_load ... lds
 //   one step ahead, swizzled unpadded tiles, one wait and one barrier per step; a third stage
 //   measured no faster and costs 25 KB of LDS per dK/dV workgroup).  Blocks are ordered
@@ -74,38 +81,9 @@ union alignas(16) BwdLds {
     DqLds<D> q;
 };
 
-// One 32 x 32 dK/dV block: P' and dS' for this wave's keys (lane) and queries (registers),
-// packed to bf16 as B operands of the dV / dK products.
-template <bool MASKED>
-__device__ inline void kv_softmax(const f32x16& s, const f32x16& dp, const float* ld, float sl2, int kloc,
-                                  int qbase, int half, bf16x8* pb, bf16x8* sb) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        const int q0 = qbase + 8 * rg + 4 * half;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(ld + ld_lsc(q0));
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(ld + ld_dlt(q0));
-        float p[4], d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e]));
-            if (MASKED && kloc > q0 + e) p[e] = 0.f;
-            d[e] = p[e] * (dp[r] - dv[e]);
-        }
-        const bf16x4 p4 = cvt4(p), d4 = cvt4(d);
-        if (rg & 1) {
-            pb[rg >> 1] = __builtin_shufflevector(pb[rg >> 1].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
-            sb[rg >> 1] = __builtin_shufflevector(sb[rg >> 1].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-            pb[rg >> 1] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
-            sb[rg >> 1] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------------------------
 // dK/dV block: keys [j0, j0 + 64) of kv head (b, g).
-template <int D>
+template <int D, bool LO>
 __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
@@ -119,7 +97,6 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int kh = w & 1, qh = w >> 1;
     const int kloc = 32 * kh + col;
     const int key = j0 + kloc;
-    const float sl2 = a.scale * kLog2e;
     const bf16* __restrict__ qrot = reinterpret_cast<const bf16*>(a.qrot);
     const bf16* __restrict__ qrot_lo = reinterpret_cast<const bf16*>(a.qrot_lo);
     const bf16* __restrict__ dout = reinterpret_cast<const bf16*>(a.dout);
@@ -128,6 +105,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int nsteps = G * nsph;
     const int hq0 = b * a.Hq + g * G;                 // first query head of the group
     const int ntile = a.Tp / kTile;                   // (l', delta) tiles per head
+    const int nblk = (T_ + kQBlk - 1) / kQBlk;        // 128-row query blocks per head (flags)
     // buffers over the group's query heads; step st covers query tile jt + st % nsph of head
     // hq0 + st / nsph (tile rows past T read another head's rows or zeros: l' = +inf there)
     const size_t hoff = (size_t)hq0 * T_ * D;
@@ -140,11 +118,20 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const unsigned lld = lds_addr(&S.ld[0][0]);
     TileCopy<D> tc;
     tc.init(w, lane);
+    // a step's low-part tile: the query block's own remainder where the forward used it, else the
+    // same buffer with size 0, whose reads land in LDS as zeros (those scores then equal the
+    // forward's)
+    const int* __restrict__ lof = a.lof + (size_t)hq0 * nblk;
     auto issue = [&](int hh, int t, int buf) {
         const unsigned row0 = (unsigned)(hh * T_ + j0 + t * kTile) * (unsigned)(D * 2);
         const unsigned so = (unsigned)buf * TileCopy<D>::kBytes;
         tc.copy(rq, row0, lq + so, w);
-        tc.copy(rql, row0, lql + so, w);
+        if constexpr (LO) {
+            const int f = __builtin_amdgcn_readfirstlane(lof[__builtin_amdgcn_readfirstlane(hh * nblk + (jt + t) / 2)]);
+            i32x4 r = rql;
+            r[2] = f ? r[2] : 0;
+            tc.copy(r, row0, lql + so, w);
+        }
         tc.copy(rg, row0, lg + so, w);
         if (lane < 8)
             copy16_to_lds(rld, (unsigned)(w * 128 + lane * 16), (unsigned)(hh * ntile + jt + t) * 512u,
@@ -197,25 +184,41 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         if (!(first && kh > qh)) {            // blocks wholly above the diagonal are skipped
             // All LDS reads of a product are issued together ahead of it (sched_barrier keeps the
             // scheduler from sinking them next to their uses, which would expose the LDS latency
-            // on every MFMA): row fragments, then S / dP; the transposed fragments of the dV / dK
-            // products are read while the softmax waits for S and dP.
+            // on every MFMA): row fragments and the accumulators' starting values (-l' and
+            // -delta of the rows: register group rg holds 4 consecutive queries), then S / dP;
+            // the transposed fragments of the dV / dK products are read while the softmax waits
+            // for S and dP.
             bf16x8 qf[NCH], qlf[NCH], gf[NCH];
+            f32x16 sacc, dp;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 qf[c] = *reinterpret_cast<const bf16x8*>(Qs + roff[c]);
-                qlf[c] = *reinterpret_cast<const bf16x8*>(Ql + roff[c]);
+                if constexpr (LO) qlf[c] = *reinterpret_cast<const bf16x8*>(Ql + roff[c]);
                 gf[c] = *reinterpret_cast<const bf16x8*>(Gs + roff[c]);
+            }
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int q0 = 32 * qh + 8 * rg + 4 * half;
+                const f32x4 nl = *reinterpret_cast<const f32x4*>(Ld + ld_lsc(q0));
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(Ld + ld_dlt(q0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sacc[4 * rg + e] = nl[e];
+                    dp[4 * rg + e] = nd[e];
+                }
+            }
+            if (first && kh == qh) {          // diagonal block: keys after the query are masked
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kloc > 32 * qh + acc_row(r, half)) sacc[r] = -INFINITY;
             }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
-            f32x16 sacc = M::mma(qf[0], kop[0], f32x16{});
-            f32x16 dp = M::mma(gf[0], vop[0], f32x16{});
-            sacc = M::mma(qlf[0], kop[0], sacc);
 #pragma unroll
-            for (int c = 1; c < NCH; ++c) {
+            for (int c = 0; c < NCH; ++c) {
                 sacc = M::mma(qf[c], kop[c], sacc);
                 dp = M::mma(gf[c], vop[c], dp);
-                sacc = M::mma(qlf[c], kop[c], sacc);
+                if constexpr (LO) sacc = M::mma(qlf[c], kop[c], sacc);
             }
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
@@ -228,11 +231,26 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                     qtf[pc][dt] = tr_frag_at<D>(Qs, trb[dt], 16 * pc);
                 }
             __builtin_amdgcn_sched_barrier(0);
+            // P' = exp2(S' - l') and dS' = P' (dP - delta) for this wave's keys (lane) and queries
+            // (registers), packed to bf16 as B operands of the dV / dK products
             bf16x8 pb[2], sb[2];
-            if (first && kh == qh)
-                kv_softmax<true>(sacc, dp, Ld, sl2, kloc, 32 * qh, half, pb, sb);
-            else
-                kv_softmax<false>(sacc, dp, Ld, sl2, kloc, 32 * qh, half, pb, sb);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                float p[4], d[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = __builtin_amdgcn_exp2f(sacc[4 * rg + e]);
+                    d[e] = p[e] * dp[4 * rg + e];
+                }
+                const bf16x4 p4 = cvt4(p), d4 = cvt4(d);
+                if (rg & 1) {
+                    pb[rg >> 1] = __builtin_shufflevector(pb[rg >> 1].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    sb[rg >> 1] = __builtin_shufflevector(sb[rg >> 1].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    pb[rg >> 1] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    sb[rg >> 1] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -265,6 +283,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     __syncthreads();
     if (qh == 0 && key < T_) {
         const float inv_scale = 1.f / a.scale;     // dV was accumulated from P' = scale * P
+        const float inv_c = 1.f / (a.scale * kLog2e);   // dK from Q~' = scale * log2(e) * Q~
         const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
         if (rope) load_acc_cs<D>(a.rope_cs, key, half, cs);
@@ -278,7 +297,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                 float x[4], y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[e] = dkt[dt][r + e] + red[((kh * NDT + dt) * 16 + r + e) * 64 + lane];
+                    x[e] = (dkt[dt][r + e] + red[((kh * NDT + dt) * 16 + r + e) * 64 + lane]) * inv_c;
                     y[e] = (dvt[dt][r + e] + red[(((2 + kh) * NDT + dt) * 16 + r + e) * 64 + lane]) * inv_scale;
                 }
                 const int d = 32 * dt + acc_row(r, half);
@@ -291,7 +310,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 
 // ---------------------------------------------------------------------------------------------
 // dQ block: queries [i0, i0 + 128) of query head (b, h).
-template <int D>
+template <int D, bool LO>
 __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
@@ -305,7 +324,6 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const int wq0 = i0 + 32 * w;            // wave's first query
     const int qrow = wq0 + col;             // this lane's query
     const size_t qoff = ((size_t)bh * T_ + min(qrow, T_ - 1)) * D;
-    const float sl2 = a.scale * kLog2e;
 
     const int kv_end = min(T_, i0 + kQBlk);
     const int nsteps = (kv_end + kTile - 1) / kTile;
@@ -323,7 +341,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     };
     issue(0, 0);
 
-    // this lane's query row: Q~ (hi and lo) and dO as B operands, l' and delta
+    // this lane's query row: Q~' (hi, and lo for a flagged block) and dO as B operands, -l' and -delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
     {
         const bf16* qr = reinterpret_cast<const bf16*>(a.qrot) + qoff + 8 * half;
@@ -332,14 +350,14 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             qop[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-            qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
+            if constexpr (LO) qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
             gop[c] = *reinterpret_cast<const bf16x8*>(gr + 16 * c);
         }
     }
     const int rowc = min(qrow, T_ - 1);
     const float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + rowc / kTile) * 2 * kTile;
-    const float lsc = ldt[ld_lsc(rowc % kTile)];
-    const float dlt = ldt[ld_dlt(rowc % kTile)];
+    const float nlsc = ldt[ld_lsc(rowc % kTile)];      // -l'
+    const float ndlt = ldt[ld_dlt(rowc % kTile)];      // -delta
     wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
@@ -383,12 +401,12 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             f32x16 sT[2], dpT[2];
             sT[0] = M::mma(kf[0][0], qop[0], f32x16{});
             dpT[0] = M::mma(vf[0][0], gop[0], f32x16{});
-            sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
+            if constexpr (LO) sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
 #pragma unroll
             for (int c = 1; c < NCH; ++c) {
                 sT[0] = M::mma(kf[0][c], qop[c], sT[0]);
                 dpT[0] = M::mma(vf[0][c], gop[c], dpT[0]);
-                sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
+                if constexpr (LO) sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
             }
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 ktf[4][NDT];
@@ -406,9 +424,9 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * rg + e;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[kt][r], sl2, -lsc));
+                    float p = __builtin_amdgcn_exp2f(sT[kt][r] + nlsc);
                     if (diag && j0 + 32 * kt + acc_row(r, half) > qrow) p = 0.f;
-                    d[e] = p * (dpT[kt][r] - dlt);
+                    d[e] = p * (dpT[kt][r] + ndlt);
                 }
                 const bf16x4 d4 = cvt4(d);
                 const int pc = 2 * kt + (rg >> 1);
@@ -420,7 +438,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
             for (int c = 0; c < NCH; ++c) {
                 sT[1] = M::mma(kf[1][c], qop[c], c == 0 ? f32x16{} : sT[1]);
                 dpT[1] = M::mma(vf[1][c], gop[c], c == 0 ? f32x16{} : dpT[1]);
-                sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
+                if constexpr (LO) sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rg = c * 4 / NCH; rg < (c + 1) * 4 / NCH; ++rg) ds_group(0, rg);
@@ -463,6 +481,28 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     }
 }
 
+// A dK/dV block uses the low-part tiles when any query block it visits (those at or after its key
+// tile, every head of its group) has its flag set; its other steps then read zeros there.
+template <int D>
+__device__ void dkdv(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
+    const int G = a.Hq / a.Hkv;
+    const int nblk = (a.T + kQBlk - 1) / kQBlk;
+    const int I0 = jt / 2, nI = nblk - I0;
+    const int* lof = a.lof + (size_t)(bg / a.Hkv * a.Hq + bg % a.Hkv * G) * nblk;
+    int any = 0;
+    for (int idx = threadIdx.x & 63; idx < G * nI; idx += 64) any |= lof[(idx / nI) * nblk + I0 + idx % nI];
+    if (__builtin_amdgcn_ballot_w64(any != 0) != 0) dkdv_block<D, true>(a, S, jt, bg);
+    else dkdv_block<D, false>(a, S, jt, bg);
+}
+
+// A dQ block uses the low part when its own query block's flag is set (as the forward did).
+template <int D>
+__device__ void dq(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
+    const int nblk = (a.T + kQBlk - 1) / kQBlk;
+    if (a.lof[(size_t)bh * nblk + qt]) dq_block<D, true>(a, S, qt, bh);
+    else dq_block<D, false>(a, S, qt, bh);
+}
+
 // workgroups per CU the kernel is compiled for: two (≤ 256 registers per wave) up to head_dim 64;
 // at 128 a dK/dV wave needs more than 256, so one
 template <int D> struct BwdOcc { static constexpr int MINB = 2; };
@@ -483,68 +523,134 @@ __global__ __launch_bounds__(kThreads, BwdOcc<D>::MINB) void bwd_bf16_kernel(Bwd
         const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
         const int gpx = BG / kXcds;                     // kv groups per XCD
         if (j < nkv * gpx) {
-            dkdv_block<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
+            dkdv<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
         } else {
             const int r = j - nkv * gpx;
             const int per = gpx * G;
             const int bg = ((r % per) / G) * kXcds + x;
-            dq_block<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
+            dq<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
         }
     } else {
         const int BH = a.B * a.Hq;
         const int ndk = nkv * BG;
         const int blk = (int)blockIdx.x;
-        if (blk < ndk) dkdv_block<D>(a, S.kv, blk / BG, blk % BG);
-        else dq_block<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
+        if (blk < ndk) dkdv<D>(a, S.kv, blk / BG, blk % BG);
+        else dq<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
     }
 }
 
-// Per query row (padded per head to Tp rows): delta = sum_d dO O and l' = L log2(e) -
-// log2(scale) (rows past T: 0 and +inf) into the tile layout of ld_lsc; Q~ = R q as bf16 hi + lo;
-// then K~ = R k (bf16).
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// Per 128-row query block of one head (b, h): -l' and -delta of its rows (delta = sum_d dO O,
+// l' = L log2(e) - log2(scale)) into the tile layout of ld_lsc, rows past T up to the end of their
+// 64-row tile getting -inf and 0.  ROT (the plain backward, whose forward kept nothing): also the
+// block's low-part flag, made as the forward makes it (max |q| over the block's raw rows against
+// the largest max |k| of the key tiles the block sees, written beforehand by key_rot_kernel), and
+// Q~' = scale log2(e) R q as bf16 hi, with the remainder lo for a flagged block.  All loads of a
+// thread are issued before any is used.
 template <int D, bool ROT>
 __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
-    constexpr int TPR = D / 8;
-    const long qrows = (long)a.B * a.Hq * a.Tp;
-    const long krows = (long)a.B * a.Hkv * a.T;
-    const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
-    const long row = gid / TPR;
-    const int part = (int)(gid % TPR);
-    if (row < qrows) {
-        const long bh = row / a.Tp;
-        const int t = (int)(row % a.Tp);
-        float sum = 0.f;
-        if (t < a.T) {
-            const size_t off = ((size_t)bh * a.T + t) * D + part * 8;
-            float o[8], d[8];
-            load16<bf16>(reinterpret_cast<const bf16*>(a.o) + off, o);
-            load16<bf16>(reinterpret_cast<const bf16*>(a.dout) + off, d);
+    constexpr int CPR = D / 8, NU = kQBlk * CPR / kThreads;   // 16-byte chunks per row / per thread
+    static_assert(NU >= 1 && kQBlk * CPR % kThreads == 0, "chunks must cover the threads evenly");
+    __shared__ float red[kThreads / 64];
+    const int T_ = a.T;
+    const int nblk = (T_ + kQBlk - 1) / kQBlk;
+    const long bh = (long)blockIdx.x / nblk;
+    const int I = (int)(blockIdx.x % nblk);
+    const int tid = threadIdx.x;
+    const size_t hbase = (size_t)bh * T_ * D;
+    const bf16* __restrict__ o = reinterpret_cast<const bf16*>(a.o) + hbase;
+    const bf16* __restrict__ g = reinterpret_cast<const bf16*>(a.dout) + hbase;
+    const bf16* __restrict__ q = reinterpret_cast<const bf16*>(a.q) + hbase;
+    bf16x8 xo[NU], xg[NU], xq[NU];
+    f32x4 cs[NU][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sum += o[e] * d[e];
+    for (int u = 0; u < NU; ++u) {
+        const int idx = u * kThreads + tid, r = idx / CPR, part = idx % CPR, t = I * kQBlk + r;
+        if (t < T_) {
+            xo[u] = *reinterpret_cast<const bf16x8*>(o + (size_t)t * D + part * 8);
+            xg[u] = *reinterpret_cast<const bf16x8*>(g + (size_t)t * D + part * 8);
             if constexpr (ROT) {
-                float q[8];
-                load16<bf16>(reinterpret_cast<const bf16*>(a.q) + off, q);
-                if (a.rope_cs) rope_rotate(q, 8, a.rope_cs, D, t, part * 8, false);
-                const bf16x8 hi = cvt8(q);
-                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot) + off) = hi;
-                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.qrot_lo) + off) = remainder8(q, hi);
+                xq[u] = *reinterpret_cast<const bf16x8*>(q + (size_t)t * D + part * 8);
+                if (a.rope_cs) {
+                    const f32x4* c = reinterpret_cast<const f32x4*>(a.rope_cs + (size_t)t * D + part * 8);
+                    cs[u][0] = c[0];
+                    cs[u][1] = c[1];
+                }
             }
         }
+    }
+    const float nlog2s = __log2f(a.scale);
 #pragma unroll
-        for (int o2 = 1; o2 < TPR; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
-        if (part == 0) {
-            float* ldt = a.ld + (row / kTile) * 2 * kTile;   // rows of a head are whole tiles (Tp)
-            const int r = t % kTile;
-            ldt[ld_lsc(r)] = t < a.T ? a.lse[bh * a.T + t] * kLog2e - __log2f(a.scale) : INFINITY;
-            ldt[ld_dlt(r)] = sum;
+    for (int u = 0; u < NU; ++u) {
+        const int idx = u * kThreads + tid, r = idx / CPR, part = idx % CPR, t = I * kQBlk + r;
+        float sum = 0.f;
+        if (t < T_) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += (float)xo[u][e] * (float)xg[u][e];
         }
-    } else if (ROT && row < qrows + krows) {
-        const long kr = row - qrows;
-        const size_t off = (size_t)kr * D + part * 8;
-        float k[8];
-        load16<bf16>(reinterpret_cast<const bf16*>(a.k) + off, k);
-        if (a.rope_cs) rope_rotate(k, 8, a.rope_cs, D, (int)(kr % a.T), part * 8, false);
-        store16<bf16>(reinterpret_cast<bf16*>(a.krot) + off, k);
+#pragma unroll
+        for (int o2 = 1; o2 < CPR; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);   // the row's CPR chunks
+        if (part == 0 && t < a.Tp) {
+            float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + t / kTile) * 2 * kTile;
+            ldt[ld_lsc(t % kTile)] = t < T_ ? nlog2s - a.lse[(size_t)bh * T_ + t] * kLog2e : -INFINITY;
+            ldt[ld_dlt(t % kTile)] = -sum;
+        }
+    }
+    if constexpr (ROT) {
+        float m = 0.f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = u * kThreads + tid, t = I * kQBlk + idx / CPR;
+            if (t < T_) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)xq[u][e]));
+            }
+        }
+        m = wave_max(m);
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        const int G = a.Hq / a.Hkv;
+        const long bg = bh / a.Hq * a.Hkv + bh % a.Hq / G;
+        const int ntk = (T_ + kTile - 1) / kTile;
+        const int nvis = min(2 * I + 2, ntk);
+        float km = 0.f;
+        for (int j = tid & 63; j < nvis; j += 64) km = fmaxf(km, a.ak[bg * ntk + j]);
+        km = wave_max(km);
+        __syncthreads();
+        float aq = red[0];
+#pragma unroll
+        for (int i = 1; i < kThreads / 64; ++i) aq = fmaxf(aq, red[i]);
+        const bool lo = a.scale * (float)D * aq * km > kLoBound;
+        if (tid == 0) a.lof[bh * nblk + I] = lo ? 1 : 0;
+        const float c = a.scale * kLog2e;
+        bf16* __restrict__ qh = reinterpret_cast<bf16*>(a.qrot) + hbase;
+        bf16* __restrict__ ql = reinterpret_cast<bf16*>(a.qrot_lo) + hbase;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = u * kThreads + tid, r = idx / CPR, part = idx % CPR, t = I * kQBlk + r;
+            if (t >= T_) continue;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (float)xq[u][e];
+            if (a.rope_cs) {
+#pragma unroll
+                for (int pr = 0; pr < 4; ++pr) {
+                    const float cc = cs[u][pr / 2][2 * (pr % 2)], sn = cs[u][pr / 2][2 * (pr % 2) + 1];
+                    const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+                    y[2 * pr] = y0 * cc - y1 * sn;
+                    y[2 * pr + 1] = y0 * sn + y1 * cc;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= c;
+            const bf16x8 hi = cvt8(y);
+            *reinterpret_cast<bf16x8*>(qh + (size_t)t * D + part * 8) = hi;
+            if (lo) *reinterpret_cast<bf16x8*>(ql + (size_t)t * D + part * 8) = remainder8(y, hi);
+        }
     }
 }
 
@@ -552,9 +658,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream, bool rotate) {
-    const long rows = (long)a.B * a.Hq * a.Tp + (rotate ? (long)a.B * a.Hkv * a.T : 0L);
-    const long threads = rows * (D / 8);
-    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    const dim3 grid((unsigned)((long)a.B * a.Hq * ((a.T + kQBlk - 1) / kQBlk)));
     if (rotate) hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();

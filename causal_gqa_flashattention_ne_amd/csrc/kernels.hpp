@@ -6,6 +6,13 @@
 
 namespace ne {
 
+// The rotated queries' low part (a second bf16 term, q~ = hi + lo) is used for a 128-query block I
+// of head (b, h) when the bound scale * D * aq128[I] * max_{j in the block's key tiles} ak64[j] on
+// its scores exceeds kLoBound: aq128 = max |q| over the block's raw query rows, ak64 = max |k| over
+// a 64-row tile of raw keys (both exact maxima of the inputs, so every kernel that recomputes them
+// reaches the same decision).  |scale q~.k~| <= scale ||q|| ||k|| <= scale * D * max|q| * max|k|.
+constexpr float kLoBound = 400.f;
+
 struct FwdArgs {
     const void* q;
     const void* k;          // bf16 kernel: keys already rotated (R k) when rope_cs is set
@@ -15,8 +22,20 @@ struct FwdArgs {
     const float* rope_cs;   // [T][D/2][2] or nullptr (bf16 kernel: used for the queries only)
     int B, Hq, Hkv, T;
     float scale;
-    void* qrot;             // bf16 kernel, training variant: the rotated queries' hi and lo bf16
-    void* qrot_lo;          // parts as the backward reads them ([B, Hq, T, D] each), or nullptr
+    void* qrot;             // bf16 kernel, training variant: the rotated queries scaled by scale *
+    void* qrot_lo;          // log2(e), hi and lo bf16 parts as the backward reads them ([B, Hq, T, D]
+                            // each; lo only for the blocks that use it), or nullptr
+    const float* ak;        // bf16 kernel: [B, Hkv, ceil(T/64)] max |k| per key tile
+    int* lof;               // bf16 kernel, training variant: [B, Hq, ceil(T/128)] low-part flags
+};
+
+// bf16 key rotation: K~ = R k (or a copy without RoPE) and ak64 per 64-row tile
+struct KeyRotArgs {
+    const void* k;          // [B, Hkv, T, D] raw keys
+    void* krot;             // [B, Hkv, T, D] rotated keys
+    float* ak;              // [B, Hkv, ceil(T/64)] max |k| per tile
+    const float* rope_cs;   // or nullptr
+    int BH, T;
 };
 
 struct BwdArgs {
@@ -31,18 +50,24 @@ struct BwdArgs {
     void* dv;
     float* delta;           // workspace (float32 path): [B, Hq, T] rowsum(dO * O)
     float* ld;              // workspace (bf16 path): per query head and 64-row tile, 4 groups of
-                            // [l' x 16 | delta x 16] (l' = L log2(e) - log2(scale); rows >= T: +inf, 0)
+                            // [-l' x 16 | -delta x 16] (l' = L log2(e) - log2(scale); rows >= T:
+                            // -l' = -inf, -delta = 0)
     float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
     float* dk_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share rotated dK / scale
     float* dv_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share dV
-    void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q rounded to bf16 (hi part)
-    void* qrot_lo;          // workspace (bf16 path): [B, Hq, T, D] bf16 remainder, rotated Q = hi + lo
+    void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q times scale*log2(e),
+                            // rounded to bf16 (hi part)
+    void* qrot_lo;          // workspace (bf16 path): [B, Hq, T, D] its bf16 remainder (written for the
+                            // blocks whose flag lof is set), hi + lo = scale*log2(e) * R q
     void* krot;             // workspace (bf16 path): [B, Hkv, T, D] rotated K, written by the preprocess
     const float* rope_cs;
     int B, Hq, Hkv, T;
     int Tp;                 // T rounded up to whole 64-row tiles
     float scale;
     int nsplit;             // float32 path: shares per key tile (bwd_f32_splits)
+    int* lof;               // bf16 path: [B, Hq, ceil(T/128)] 1 where a 128-row query block uses the
+                            // rotated queries' low part (the forward's decision, kLoBound)
+    float* ak;              // bf16 path: [B, Hkv, ceil(T/64)] max |k| per 64-row key tile
 };
 
 // float32 backward: each workgroup owns 128 keys of one (batch, kv head) and one of nsplit
@@ -115,6 +140,7 @@ template <typename T, int D> hipError_t launch_bwd_pre(const BwdArgs& a, hipStre
 template <typename T, int D> hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 // a.qrot set: also writes the rotated queries (hi and lo parts) for the backward
 template <int D> hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_key_rot(const KeyRotArgs& a, hipStream_t stream);
 // rotate == false: only the per-row (l', delta) data; the rotated queries and keys are already in
 // the workspace (written by the training forward)
 template <int D> hipError_t launch_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream, bool rotate = true);

@@ -108,11 +108,13 @@ def test_workspace_size_and_check():
     need = ne.bwd_workspace_bytes(p)
     delta = 2 * 4 * 16 * 4
     rows_padded = 2 * 4 * 64         # bf16: rows of each head padded to whole 64-row tiles
-    # bf16: (l', delta) per padded row | rotated Q hi | rotated Q lo | rotated K
+    # bf16: (-l', -delta) per padded row | low-part flag per 128-row query block (256-byte
+    # aligned) | max |k| per 64-row key tile (aligned) | scaled rotated Q hi | its lo | rotated K
     # float32: delta | float32 dQ accumulator | one dK and one dV slice per share of a key tile
     # (128 keys; shares: enough for ~1024 workgroups, at most one 32-query step each: here
     # 4 key-tile units and 2 steps per unit, so 2 shares)
-    assert need == rows_padded * 2 * 4 + 2 * (2 * 4 * 16 * 64 * 2) + 2 * 2 * 16 * 64 * 2
+    assert need == rows_padded * 2 * 4 + 256 + 256 + 2 * (2 * 4 * 16 * 64 * 2) + 2 * 2 * 16 * 64 * 2
+    # the forward's: max |k| per key tile (aligned), then the rotated keys when there is RoPE
     pf = params(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_F32)
     shares = 2
     assert ne.bwd_workspace_bytes(pf) == ((delta + 255) // 256) * 256 + (2 * 4 + 2 * shares * 2 * 2) * 16 * 64 * 4
@@ -143,10 +145,11 @@ def test_rope_entry_points_validate():
 
 def test_forward_workspace():
     p = params(B=2, Hq=4, Hkv=2, T=16, D=64)
-    assert ne.fwd_workspace_bytes(p) == 0                 # no RoPE: the keys are used as given
+    assert ne.fwd_workspace_bytes(p) == 256               # no RoPE: max |k| per key tile only
+    assert fwd(p, ws=0) == -1
     p.rope_cs, p.rope_rows = ALIGNED, 16
     need = ne.fwd_workspace_bytes(p)
-    assert need == 2 * 2 * 16 * 64 * 2                    # bf16 rotated keys, rotated once per call
+    assert need == 256 + 2 * 2 * 16 * 64 * 2              # and the bf16 rotated keys, rotated once per call
     assert fwd(p, ws=0) == -1
     assert fwd(p, ws=MISALIGNED) == -4
     assert fwd(p, ws_bytes=need - 1) == -5

@@ -79,8 +79,11 @@ def test_decode_rope_off_and_scale(theta, scale):
 
 
 def test_decode_matches_forward_last_rows():
-    """The library's decode on a cache filled by ne_rope_apply equals the library's own forward at
-    the last n positions (same bf16 rotation of the keys, same query hi/lo split)."""
+    """The library's decode on a cache filled by ne_rope_apply agrees with the library's own forward
+    at the last n positions: the same bf16 rotation of the keys.  The decode always carries the
+    query as bf16 hi + lo; the forward drops the low part for blocks whose score bound is under
+    kLoBound (as here), so the two differ by the query's bf16 rounding in the scores: about 2^-9 of
+    a score of a few units, ~1e-4 of L's scale (bar 1e-3), ~1e-3 of O's (bar 1e-2)."""
     dev = torch.device("cuda:0")
     B, Hq, Hkv, T, D, n = 2, 12, 4, 320, 64, 3
     q, k, v, _ = gen.small_case(31, B, Hq, Hkv, T, D, "bf16")
@@ -92,7 +95,7 @@ def test_decode_matches_forward_last_rows():
     e_o = (o_d.float() - o_f[:, :, T - n:].float()).abs().max().item() / o_f.float().abs().max().item()
     e_l = (l_d - l_f[:, :, T - n:]).abs().max().item() / l_f.abs().max().item()
     log("  decode vs forward: e(O) %.2e e(L) %.2e" % (e_o, e_l))
-    assert e_o <= 1e-2 and e_l <= 1e-4
+    assert e_o <= 1e-2 and e_l <= 1e-3
 
 
 def test_decode_deterministic():
