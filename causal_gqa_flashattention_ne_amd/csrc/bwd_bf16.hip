@@ -121,13 +121,17 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     // a step's low-part tile: the query block's own remainder where the forward used it, else the
     // same buffer with size 0, whose reads land in LDS as zeros (those scores then equal the
     // forward's)
-    const int* __restrict__ lof = a.lof + (size_t)hq0 * nblk;
+    // the flags are read through the constant address space: scalar loads, which do not share
+    // the vector-memory counter with the tile copies in flight (a vector load there would be
+    // waited for with vmcnt(0), i.e. after every copy issued so far)
+    typedef const __attribute__((address_space(4))) int cint;
+    cint* lof = (cint*)(unsigned long long)(a.lof + (size_t)hq0 * nblk);
     auto issue = [&](int hh, int t, int buf) {
         const unsigned row0 = (unsigned)(hh * T_ + j0 + t * kTile) * (unsigned)(D * 2);
         const unsigned so = (unsigned)buf * TileCopy<D>::kBytes;
         tc.copy(rq, row0, lq + so, w);
         if constexpr (LO) {
-            const int f = __builtin_amdgcn_readfirstlane(lof[__builtin_amdgcn_readfirstlane(hh * nblk + (jt + t) / 2)]);
+            const int f = lof[__builtin_amdgcn_readfirstlane(hh * nblk + (jt + t) / 2)];
             i32x4 r = rql;
             r[2] = f ? r[2] : 0;
             tc.copy(r, row0, lql + so, w);

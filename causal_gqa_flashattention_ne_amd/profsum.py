@@ -27,7 +27,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNELS = {"fwd_bf16_kernel": "fwd", "bwd_pre_bf16_kernel": "bwd_pre", "bwd_bf16_kernel": "bwd_main",
            "fwd_kernel": "fwd", "bwd_pre_kernel": "bwd_pre", "bwd_main_kernel": "bwd_main",
-           "rope_apply_kernel": "rope_keys", "decode_split_kernel": "decode_split",
+           "rope_apply_kernel": "rope_keys", "key_rot_kernel": "key_rot", "decode_split_kernel": "decode_split",
            "decode_merge_kernel": "decode_merge", "decode16_kernel": "decode16",
            "proj_kernel": "qkv_proj"}
 CAL_BYTES = 256 << 20
@@ -38,7 +38,7 @@ CAL_BYTES = 256 << 20
 _HEADERS = ("common.hpp", "tiles.hpp", "kernels.hpp")
 KERNEL_SOURCES = {
     "fwd": ("fwd_bf16.hip", "fwd.hip"), "bwd_pre": ("bwd_bf16.hip", "bwd.hip"), "bwd_main": ("bwd_bf16.hip", "bwd.hip"),
-    "rope_keys": ("rope.hip",), "decode16": ("decode.hip",), "decode_split": ("decode.hip",),
+    "rope_keys": ("rope.hip",), "key_rot": ("fwd_bf16.hip",), "decode16": ("decode.hip",), "decode_split": ("decode.hip",),
     "decode_merge": ("decode.hip",), "qkv_proj": ("proj.hip",),
 }
 
