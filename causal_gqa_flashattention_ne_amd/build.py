@@ -24,7 +24,6 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay disabled: the kernels use ordinary scalar float arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -384,13 +384,15 @@ int ne_qkv_proj(const ne_qkv_params* p, const void* x, const void* w, void* q, v
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     const size_t qe = (size_t)p->B * p->Hq * p->T * p->D, ke = (size_t)p->B * p->Hkv * p->T * p->D;
-    // float32: delta | float32 dQ accumulator | dK and dV slices, one per share of a key tile
+    // float32: delta | dQ parts, one slice per 128-key tile | dK and dV slices, one per share of a
+    // key tile
     // bf16: (-l', -delta) per row | low-part flags | max |k| per key tile | scaled rotated Q hi | lo |
     // rotated K
     if (p->dtype == NE_DTYPE_BF16)
         return delta_bytes(p) + lo_flag_bytes(p) + key_bound_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
     const size_t ns = (size_t)ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
-    return delta_bytes(p) + (qe + 2 * ns * ke) * sizeof(float);
+    const size_t nkt = (size_t)(p->T + ne::kBwdF32Keys - 1) / ne::kBwdF32Keys;
+    return delta_bytes(p) + (nkt * qe + 2 * ns * ke) * sizeof(float);
 }
 
 namespace {
@@ -430,7 +432,7 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
         const size_t ke = (size_t)p->B * p->Hkv * p->T * p->D;
         nsplit = ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
         dq_acc = reinterpret_cast<float*>(ws + delta_bytes(p));
-        dk_acc = dq_acc + qe;
+        dk_acc = dq_acc + (size_t)((p->T + ne::kBwdF32Keys - 1) / ne::kBwdF32Keys) * qe;
         dv_acc = dk_acc + (size_t)nsplit * ke;
     }
     *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, dk_acc, dv_acc, qrot, qrot_lo, krot, p->rope_cs,

@@ -2,7 +2,7 @@
 // in fwd.hip; ai-paper-delta NanoEuler page, "Core Mechanics").
 //
 // Three launches:
-//   1. bwd_pre:  delta_i = sum_d dO_id * O_id  (float32), and the float32 dQ accumulator zeroed.
+//   1. bwd_pre:  delta_i = sum_d dO_id * O_id  (float32).
 //   2. bwd_main: key/value-tile major.  A workgroup owns BN = 128 keys of one (batch, kv head)
 //      and one contiguous share of that tile's steps; wave w owns keys [32w, 32w + 32).  The
 //      steps are every (query head of the kv group, query tile at or after the tile's first key)
@@ -10,16 +10,19 @@
 //      as make about a thousand workgroups (one share at long sequences), so that short
 //      sequences still fill the GPU (bwd_f32_splits).  Each step recomputes
 //          S = Q~ K~^T,  P = exp(scale*S - L),  dP = dO V^T,  dS = P * (dP - delta),
-//          dV^T += dO^T P,  dK~^T += Q~^T dS,  dQ~ += dS K~ (float32 atomics, scale applied).
+//          dV^T += dO^T P,  dK~^T += Q~^T dS,  dQ~_tile = dS K~ (scale applied).
 //      S is formed untransposed here, so one lane owns one key: P and dS are then the B operands
 //      of the dV^T / dK^T products directly from the accumulator registers (the K order of those
 //      products is the accumulator's row order, and Q^T / dO^T are read from LDS in that order).
 //      dS goes through LDS once per step so that all four waves' keys feed the dQ product.
 //      dK~ and dV of the share are summed in registers (the group sum over query heads) and
-//      stored into the share's own workspace slice; an empty share stores zeros.
-//   3. bwd_dq:   dQ = R^T dQ~, and dK = R^T (scale sum of the dK~ slices) and dV = sum of the dV
-//      slices, converted to the element type (R^T is linear, so un-rotating the sum equals summing
-//      the un-rotated shares; the slices are added in share order, so dK and dV are deterministic).
+//      stored into the share's own workspace slice; an empty share stores zeros.  A key tile's
+//      contribution to dQ~ of the step's queries is stored (plain stores) into that key tile's own
+//      dQ slice: each element of a slice has exactly one writer (one step of one share, one wave).
+//   3. bwd_dq:   dQ = R^T (sum of the dQ~ slices of key tiles 0 .. the row's own), and
+//      dK = R^T (scale sum of the dK~ slices) and dV = sum of the dV slices, converted to the
+//      element type (R^T is linear, so un-rotating the sum equals summing the un-rotated parts).
+//      Every sum is taken in slice order, so dQ, dK and dV are deterministic (no atomics).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,9 +59,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
         load16<T>(reinterpret_cast<const T*>(a.dout) + row * D + part * VEC, d);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) sum += o[e] * d[e];
-        float* acc = a.dq_acc + row * D + part * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) *reinterpret_cast<f32x4*>(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
@@ -285,11 +285,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
                     }
                     acc = M::mma(sa, kb, acc);
                 }
-                float* __restrict__ dqa = a.dq_acc + (hrow + i0) * D + 32 * dt + col;
+                // this key tile's slice of the dQ~ parts (rows at or after the tile's first key)
+                float* __restrict__ dqa = a.dq_acc + (size_t)jt * a.B * a.Hq * T_ * D + (hrow + i0) * D + 32 * dt + col;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int qr = 32 * qt + acc_row(r, half);
-                    if (i0 + qr < T_) unsafeAtomicAdd(dqa + (size_t)qr * D, acc[r] * a.scale);
+                    if (i0 + qr < T_) dqa[(size_t)qr * D] = acc[r] * a.scale;
                 }
             }
         }
@@ -336,7 +337,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     }
     const long row = gid / (D / 4);
     const int d0 = (int)(gid % (D / 4)) * 4;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.dq_acc + row * D + d0);
+    // the dQ~ parts of key tiles 0 .. the row's own tile, in tile order
+    const int last = (int)(row % a.T) / kBwdBN;
+    const size_t slice = (size_t)a.B * a.Hq * a.T * D;
+    f32x4 v = *reinterpret_cast<const f32x4*>(a.dq_acc + row * D + d0);
+    for (int kt = 1; kt <= last; ++kt) v += *reinterpret_cast<const f32x4*>(a.dq_acc + kt * slice + row * D + d0);
     float x[4] = {v[0], v[1], v[2], v[3]};
     if (a.rope_cs) rope_rotate(x, 4, a.rope_cs, D, (int)(row % a.T), d0, true);
     store4<T>(reinterpret_cast<T*>(a.dq) + row * D + d0, x[0], x[1], x[2], x[3]);

@@ -52,7 +52,8 @@ struct BwdArgs {
     float* ld;              // workspace (bf16 path): per query head and 64-row tile, 4 groups of
                             // [-l' x 16 | -delta x 16] (l' = L log2(e) - log2(scale); rows >= T:
                             // -l' = -inf, -delta = 0)
-    float* dq_acc;          // workspace (float32 path): [B, Hq, T, D] accumulator of rotated dQ
+    float* dq_acc;          // workspace (float32 path): [ceil(T/128)][B, Hq, T, D] rotated dQ parts,
+                            // one slice per 128-key tile (rows at or after the tile's first key)
     float* dk_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share rotated dK / scale
     float* dv_acc;          // workspace (float32 path): [nsplit][B, Hkv, T, D] per-share dV
     void* qrot;             // workspace (bf16 path): [B, Hq, T, D] rotated Q times scale*log2(e),

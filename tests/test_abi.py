@@ -110,17 +110,17 @@ def test_workspace_size_and_check():
     rows_padded = 2 * 4 * 64         # bf16: rows of each head padded to whole 64-row tiles
     # bf16: (-l', -delta) per padded row | low-part flag per 128-row query block (256-byte
     # aligned) | max |k| per 64-row key tile (aligned) | scaled rotated Q hi | its lo | rotated K
-    # float32: delta | float32 dQ accumulator | one dK and one dV slice per share of a key tile
-    # (128 keys; shares: enough for ~1024 workgroups, at most one 32-query step each: here
+    # float32: delta | one dQ slice per 128-key tile | one dK and one dV slice per share of a key
+    # tile (128 keys; shares: enough for ~1024 workgroups, at most one 32-query step each: here
     # 4 key-tile units and 2 steps per unit, so 2 shares)
     assert need == rows_padded * 2 * 4 + 256 + 256 + 2 * (2 * 4 * 16 * 64 * 2) + 2 * 2 * 16 * 64 * 2
     # the forward's: max |k| per key tile (aligned), then the rotated keys when there is RoPE
     pf = params(B=2, Hq=4, Hkv=2, T=16, D=64, dtype_code=ne.NE_DTYPE_F32)
     shares = 2
     assert ne.bwd_workspace_bytes(pf) == ((delta + 255) // 256) * 256 + (2 * 4 + 2 * shares * 2 * 2) * 16 * 64 * 4
-    # long sequences: one share per key tile (the tiles alone are >= 1024 workgroups)
+    # long sequences: one share per key tile (the tiles alone are >= 1024 workgroups); 16 dQ slices
     pl = params(B=8, Hq=8, Hkv=8, T=2048, D=64, dtype_code=ne.NE_DTYPE_F32)
-    assert ne.bwd_workspace_bytes(pl) == 8 * 8 * 2048 * 4 + (8 * 8 + 2 * 8 * 8) * 2048 * 64 * 4
+    assert ne.bwd_workspace_bytes(pl) == 8 * 8 * 2048 * 4 + (16 * 8 * 8 + 2 * 8 * 8) * 2048 * 64 * 4
     assert bwd(p, ws_bytes=need - 1) == -5
 
 

@@ -62,7 +62,7 @@ def short_waits(asm_lines, need=5):
 def compile_asm(src, outdir):
     out = os.path.join(outdir, src + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-munsafe-fp-atomics", "-I" + os.path.join(ROOT, "include"), "--offload-device-only",
+           "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "--offload-device-only",
            "-S", os.path.join(CSRC, src), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     with open(out) as f:
