@@ -45,6 +45,8 @@
 #include "kernels.hpp"
 #include "tiles.hpp"
 
+#include <type_traits>
+
 namespace ne {
 
 namespace {
@@ -67,12 +69,14 @@ struct alignas(16) DkdvLds {
     alignas(16) bf16 ql[kBS][kTile * D];   // Q~ remainder tiles (lo part)
     alignas(16) bf16 g[kBS][kTile * D];    // dO tiles
     alignas(16) float ld[kBS][2 * kTile];  // l' and delta, see ld_lsc
+    alignas(16) float cs[kTile * D];       // RoPE table rows of the block's keys (CsRows layout)
 };
 
 template <int D>
 struct alignas(16) DqLds {
     alignas(16) bf16 k[kBS][kTile * D];    // K~ tiles [key][d]
     alignas(16) bf16 v[kBS][kTile * D];    // V tiles
+    alignas(16) float cs[kQBlk * D];       // RoPE table rows of the block's queries (CsRows layout)
 };
 
 template <int D>
@@ -81,9 +85,43 @@ union alignas(16) BwdLds {
     DqLds<D> q;
 };
 
+// ROWS rows of the RoPE table ((cos, sin) pairs, D floats per row) copied into LDS with the copy
+// instructions of the tiles, in the prologue, for the un-rotation in the epilogue; the 16-byte
+// chunk c of row r sits at chunk position c ^ (r mod D/4), so that the epilogue's reads (one row
+// per lane) are spread over the banks.  Rows past the table's end read as zeros.
+template <int D, int ROWS>
+struct CsRows {
+    static constexpr int CPR = D / 4, NU = ROWS * CPR / (64 * kWaves);
+    static_assert(NU >= 1 && (ROWS * CPR) % (64 * kWaves) == 0, "table chunks must cover the waves evenly");
+    __device__ static inline void copy(const float* cs, int T, int r0, unsigned lds, int w, int lane) {
+        const i32x4 rs = buffer_rsrc(cs, (unsigned)T * (unsigned)(D * 4));
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = (u * kWaves + w) * 64 + lane, r = idx / CPR, c = (idx % CPR) ^ (r % CPR);
+            copy16_to_lds(rs, (unsigned)(r * D + 4 * c) * 4u, (unsigned)r0 * (unsigned)(D * 4), lds + (unsigned)(u * kWaves + w) * 1024u);
+        }
+    }
+    // element offset of (row r, d), d a multiple of 4 (one 16-byte chunk)
+    __device__ static inline int at(int r, int d) { return r * D + (((d >> 2) ^ (r % CPR)) << 2); }
+    // the table entries behind this lane's accumulator groups of row r (see load_acc_cs)
+    __device__ static inline void read(const float* S, int r, int half, f32x4 (&c)[D / 32][4]) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) c[dt][rq] = *reinterpret_cast<const f32x4*>(S + at(r, 32 * dt + acc_row(4 * rq, half)));
+    }
+};
+
+typedef const __attribute__((address_space(4))) int cint;   // loads through it are scalar loads
+
 // ---------------------------------------------------------------------------------------------
 // dK/dV block: keys [j0, j0 + 64) of kv head (b, g).
-template <int D, bool LO>
+//
+// Prologue: every load the block needs before its first step goes out together (the low-part
+// flags of the query blocks it meets, this lane's K~ / V rows, the first tiles, the RoPE rows of
+// the epilogue), so that the block waits for one memory round trip; only a block that uses the
+// low part then fetches its first remainder tile.
+template <int D>
 __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
@@ -106,6 +144,11 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const int hq0 = b * a.Hq + g * G;                 // first query head of the group
     const int ntile = a.Tp / kTile;                   // (l', delta) tiles per head
     const int nblk = (T_ + kQBlk - 1) / kQBlk;        // 128-row query blocks per head (flags)
+    // the low-part flags of the query blocks the key tile meets: head hh, blocks I0 + i; lane
+    // hh * nI + i loads one (the load stays in flight until the ballot below)
+    const int I0 = jt / 2, nI = nblk - I0, nfl = G * nI;
+    const int* lofh = a.lof + (size_t)hq0 * nblk;
+    const int f0 = lane < nfl ? lofh[(lane / nI) * nblk + I0 + lane % nI] : 0;
     // buffers over the group's query heads; step st covers query tile jt + st % nsph of head
     // hq0 + st / nsph (tile rows past T read another head's rows or zeros: l' = +inf there)
     const size_t hoff = (size_t)hq0 * T_ * D;
@@ -118,32 +161,28 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     const unsigned lld = lds_addr(&S.ld[0][0]);
     TileCopy<D> tc;
     tc.init(w, lane);
-    // a step's low-part tile: the query block's own remainder where the forward used it, else the
-    // same buffer with size 0, whose reads land in LDS as zeros (those scores then equal the
-    // forward's)
-    // the flags are read through the constant address space: scalar loads, which do not share
-    // the vector-memory counter with the tile copies in flight (a vector load there would be
-    // waited for with vmcnt(0), i.e. after every copy issued so far)
-    typedef const __attribute__((address_space(4))) int cint;
-    cint* lof = (cint*)(unsigned long long)(a.lof + (size_t)hq0 * nblk);
+    // the tiles of step (head hh, query tile jt + t) that every block reads: Q~ hi, dO, (l', delta)
     auto issue = [&](int hh, int t, int buf) {
         const unsigned row0 = (unsigned)(hh * T_ + j0 + t * kTile) * (unsigned)(D * 2);
         const unsigned so = (unsigned)buf * TileCopy<D>::kBytes;
         tc.copy(rq, row0, lq + so, w);
-        if constexpr (LO) {
-            const int f = lof[__builtin_amdgcn_readfirstlane(hh * nblk + (jt + t) / 2)];
-            i32x4 r = rql;
-            r[2] = f ? r[2] : 0;
-            tc.copy(r, row0, lql + so, w);
-        }
         tc.copy(rg, row0, lg + so, w);
         if (lane < 8)
             copy16_to_lds(rld, (unsigned)(w * 128 + lane * 16), (unsigned)(hh * ntile + jt + t) * 512u,
                           lld + (unsigned)(buf * 512 + w * 128));
     };
+    // a step's low-part tile: the query block's own remainder where the forward used it (flag f),
+    // else the same buffer with size 0, whose reads land in LDS as zeros (those scores then equal
+    // the forward's)
+    auto issue_lo = [&](int hh, int t, int buf, int f) {
+        const unsigned row0 = (unsigned)(hh * T_ + j0 + t * kTile) * (unsigned)(D * 2);
+        i32x4 r = rql;
+        r[2] = __builtin_amdgcn_readfirstlane(f ? r[2] : 0);
+        tc.copy(r, row0, lql + (unsigned)buf * TileCopy<D>::kBytes, w);
+    };
     issue(0, 0, 0);
-    int ih = 0, it = 1;                               // head / tile of the next step to issue
-    if (it == nsph) { it = 0; ++ih; }
+    const bool rope = a.rope_cs != nullptr;
+    if (rope) CsRows<D, kTile>::copy(a.rope_cs, T_, j0, lds_addr(&S.cs[0]), w, lane);
 
     // this lane's key row: K~ and V as B operands
     bf16x8 kop[NCH], vop[NCH];
@@ -157,7 +196,23 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
             vop[c] = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
         }
     }
-    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
+    // A block uses the low-part tiles when any query block it meets has its flag set; its other
+    // steps then read zeros there.  With at most 64 such blocks their flags are one wave-uniform
+    // mask (bit hh * nI + i); beyond that a step reads its flag with a scalar load (these do not
+    // share the vector-memory counter with the tile copies in flight: a vector load in the loop
+    // would be waited for with vmcnt(0), i.e. after every copy issued so far).
+    int fl = f0;
+    for (int idx = lane + 64; idx < nfl; idx += 64) fl |= lofh[(idx / nI) * nblk + I0 + idx % nI];
+    const unsigned long long fmask = __builtin_amdgcn_ballot_w64(f0 != 0);
+    const bool lo = __builtin_amdgcn_ballot_w64(fl != 0) != 0;
+    cint* lofs = (cint*)(unsigned long long)lofh;
+    auto flag = [&](int hh, int t) -> int {
+        const int i = (jt + t) / 2 - I0;
+        if (nfl <= 64) return (int)((fmask >> (hh * nI + i)) & 1ull);
+        return lofs[__builtin_amdgcn_readfirstlane(hh * nblk + I0 + i)];
+    };
+    if (lo) issue_lo(0, 0, 0, flag(0, 0));
+    wait_vmcnt<0>();   // operands, the first tiles and the table rows (see copy16_to_lds)
 
     // per-lane LDS offsets of the row fragments (query row 32*qh + col, chunks 2c + half)
     int roff[NCH];
@@ -172,103 +227,112 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) { dkt[i] = f32x16{}; dvt[i] = f32x16{}; }
 
-    int buf = 0, ct = 0;                              // stage and query tile of the current step
-    for (int st = 0; st < nsteps; ++st) {
-        wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
-        step_barrier();                      // tile st is complete; the other stage is free
-        if (st + 1 < nsteps) {
-            issue(ih, it, buf ^ 1);
-            if (++it == nsph) { it = 0; ++ih; }
+    // the step loop, with and without the low-part products
+    auto run = [&](auto lo_c) {
+        constexpr bool LO = decltype(lo_c)::value;
+        int ih = 0, it = 1;                           // head / tile of the next step to issue
+        if (it == nsph) { it = 0; ++ih; }
+        int buf = 0, ct = 0;                          // stage and query tile of the current step
+        for (int st = 0; st < nsteps; ++st) {
+            wait_vmcnt<0>();                 // this wave's copies of tile st, the only ones in flight
+            step_barrier();                  // tile st is complete; the other stage is free
+            if (st + 1 < nsteps) {
+                issue(ih, it, buf ^ 1);
+                if constexpr (LO) issue_lo(ih, it, buf ^ 1, flag(ih, it));
+                if (++it == nsph) { it = 0; ++ih; }
+            }
+            const bf16* Qs = S.q[buf];
+            const bf16* Ql = S.ql[buf];
+            const bf16* Gs = S.g[buf];
+            const float* Ld = S.ld[buf];
+            const bool first = ct == 0;
+            if (!(first && kh > qh)) {        // blocks wholly above the diagonal are skipped
+                // All LDS reads of a product are issued together ahead of it (sched_barrier keeps
+                // the scheduler from sinking them next to their uses, which would expose the LDS
+                // latency on every MFMA): row fragments and the accumulators' starting values (-l'
+                // and -delta of the rows: register group rg holds 4 consecutive queries), then S /
+                // dP; the transposed fragments of the dV / dK products are read while the softmax
+                // waits for S and dP.
+                bf16x8 qf[NCH], qlf[NCH], gf[NCH];
+                f32x16 sacc, dp;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    qf[c] = *reinterpret_cast<const bf16x8*>(Qs + roff[c]);
+                    if constexpr (LO) qlf[c] = *reinterpret_cast<const bf16x8*>(Ql + roff[c]);
+                    gf[c] = *reinterpret_cast<const bf16x8*>(Gs + roff[c]);
+                }
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int q0 = 32 * qh + 8 * rg + 4 * half;
+                    const f32x4 nl = *reinterpret_cast<const f32x4*>(Ld + ld_lsc(q0));
+                    const f32x4 nd = *reinterpret_cast<const f32x4*>(Ld + ld_dlt(q0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sacc[4 * rg + e] = nl[e];
+                        dp[4 * rg + e] = nd[e];
+                    }
+                }
+                if (first && kh == qh) {      // diagonal block: keys after the query are masked
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kloc > 32 * qh + acc_row(r, half)) sacc[r] = -INFINITY;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    sacc = M::mma(qf[c], kop[c], sacc);
+                    dp = M::mma(gf[c], vop[c], dp);
+                    if constexpr (LO) sacc = M::mma(qlf[c], kop[c], sacc);
+                }
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 gt[2][NDT], qtf[2][NDT];
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        gt[pc][dt] = tr_frag_at<D>(Gs, trb[dt], 16 * pc);
+                        qtf[pc][dt] = tr_frag_at<D>(Qs, trb[dt], 16 * pc);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+                // P' = exp2(S' - l') and dS' = P' (dP - delta) for this wave's keys (lane) and
+                // queries (registers), packed to bf16 as B operands of the dV / dK products
+                bf16x8 pb[2], sb[2];
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    float p[4], d[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p[e] = __builtin_amdgcn_exp2f(sacc[4 * rg + e]);
+                        d[e] = p[e] * dp[4 * rg + e];
+                    }
+                    const bf16x4 p4 = cvt4(p), d4 = cvt4(d);
+                    if (rg & 1) {
+                        pb[rg >> 1] = __builtin_shufflevector(pb[rg >> 1].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        sb[rg >> 1] = __builtin_shufflevector(sb[rg >> 1].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+                        pb[rg >> 1] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        sb[rg >> 1] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        dvt[dt] = M::mma(gt[pc][dt], pb[pc], dvt[dt]);
+                        dkt[dt] = M::mma(qtf[pc][dt], sb[pc], dkt[dt]);
+                    }
+                __builtin_amdgcn_s_setprio(0);
+            }
+            buf ^= 1;
+            if (++ct == nsph) ct = 0;
         }
-        const bf16* Qs = S.q[buf];
-        const bf16* Ql = S.ql[buf];
-        const bf16* Gs = S.g[buf];
-        const float* Ld = S.ld[buf];
-        const bool first = ct == 0;
-        if (!(first && kh > qh)) {            // blocks wholly above the diagonal are skipped
-            // All LDS reads of a product are issued together ahead of it (sched_barrier keeps the
-            // scheduler from sinking them next to their uses, which would expose the LDS latency
-            // on every MFMA): row fragments and the accumulators' starting values (-l' and
-            // -delta of the rows: register group rg holds 4 consecutive queries), then S / dP;
-            // the transposed fragments of the dV / dK products are read while the softmax waits
-            // for S and dP.
-            bf16x8 qf[NCH], qlf[NCH], gf[NCH];
-            f32x16 sacc, dp;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                qf[c] = *reinterpret_cast<const bf16x8*>(Qs + roff[c]);
-                if constexpr (LO) qlf[c] = *reinterpret_cast<const bf16x8*>(Ql + roff[c]);
-                gf[c] = *reinterpret_cast<const bf16x8*>(Gs + roff[c]);
-            }
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int q0 = 32 * qh + 8 * rg + 4 * half;
-                const f32x4 nl = *reinterpret_cast<const f32x4*>(Ld + ld_lsc(q0));
-                const f32x4 nd = *reinterpret_cast<const f32x4*>(Ld + ld_dlt(q0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sacc[4 * rg + e] = nl[e];
-                    dp[4 * rg + e] = nd[e];
-                }
-            }
-            if (first && kh == qh) {          // diagonal block: keys after the query are masked
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kloc > 32 * qh + acc_row(r, half)) sacc[r] = -INFINITY;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                sacc = M::mma(qf[c], kop[c], sacc);
-                dp = M::mma(gf[c], vop[c], dp);
-                if constexpr (LO) sacc = M::mma(qlf[c], kop[c], sacc);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 gt[2][NDT], qtf[2][NDT];
-#pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    gt[pc][dt] = tr_frag_at<D>(Gs, trb[dt], 16 * pc);
-                    qtf[pc][dt] = tr_frag_at<D>(Qs, trb[dt], 16 * pc);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // P' = exp2(S' - l') and dS' = P' (dP - delta) for this wave's keys (lane) and queries
-            // (registers), packed to bf16 as B operands of the dV / dK products
-            bf16x8 pb[2], sb[2];
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                float p[4], d[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(sacc[4 * rg + e]);
-                    d[e] = p[e] * dp[4 * rg + e];
-                }
-                const bf16x4 p4 = cvt4(p), d4 = cvt4(d);
-                if (rg & 1) {
-                    pb[rg >> 1] = __builtin_shufflevector(pb[rg >> 1].lo, p4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    sb[rg >> 1] = __builtin_shufflevector(sb[rg >> 1].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-                } else {
-                    pb[rg >> 1] = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    sb[rg >> 1] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    dvt[dt] = M::mma(gt[pc][dt], pb[pc], dvt[dt]);
-                    dkt[dt] = M::mma(qtf[pc][dt], sb[pc], dkt[dt]);
-                }
-            __builtin_amdgcn_s_setprio(0);
-        }
-        buf ^= 1;
-        if (++ct == nsph) ct = 0;
-    }
+    };
+    if (lo) run(std::true_type{});
+    else run(std::false_type{});
 
     // add the two query halves' partial dK^T / dV^T through LDS (reuses the tile buffers once
     // every wave is past its last step)
@@ -288,9 +352,8 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     if (qh == 0 && key < T_) {
         const float inv_scale = 1.f / a.scale;     // dV was accumulated from P' = scale * P
         const float inv_c = 1.f / (a.scale * kLog2e);   // dK from Q~' = scale * log2(e) * Q~
-        const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) load_acc_cs<D>(a.rope_cs, key, half, cs);
+        if (rope) CsRows<D, kTile>::read(S.cs, kloc, half, cs);
         const size_t base = ((size_t)bg * T_ + key) * D;
         bf16* __restrict__ dk = reinterpret_cast<bf16*>(a.dk) + base;
         bf16* __restrict__ dv = reinterpret_cast<bf16*>(a.dv) + base;
@@ -313,8 +376,11 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ block: queries [i0, i0 + 128) of query head (b, h).
-template <int D, bool LO>
+// dQ block: queries [i0, i0 + 128) of query head (b, h).  As in the dK/dV block, the prologue's
+// loads (the block's low-part flag, the first key / value tiles, this lane's Q~' and dO rows and
+// (l', delta), the RoPE rows) go out together; a block that uses the low part (as the forward
+// did for it) then loads its remainder rows.
+template <int D>
 __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
@@ -328,6 +394,8 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const int wq0 = i0 + 32 * w;            // wave's first query
     const int qrow = wq0 + col;             // this lane's query
     const size_t qoff = ((size_t)bh * T_ + min(qrow, T_ - 1)) * D;
+    const int nblk = (T_ + kQBlk - 1) / kQBlk;
+    const int flag = ((cint*)(unsigned long long)a.lof)[(size_t)bh * nblk + qt];   // scalar load
 
     const int kv_end = min(T_, i0 + kQBlk);
     const int nsteps = (kv_end + kTile - 1) / kTile;
@@ -344,17 +412,17 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         tc.copy(rv, row0, lv + so, w);
     };
     issue(0, 0);
+    const bool rope = a.rope_cs != nullptr;
+    if (rope) CsRows<D, kQBlk>::copy(a.rope_cs, T_, i0, lds_addr(&S.cs[0]), w, lane);
 
     // this lane's query row: Q~' (hi, and lo for a flagged block) and dO as B operands, -l' and -delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
     {
         const bf16* qr = reinterpret_cast<const bf16*>(a.qrot) + qoff + 8 * half;
-        const bf16* ql = reinterpret_cast<const bf16*>(a.qrot_lo) + qoff + 8 * half;
         const bf16* gr = reinterpret_cast<const bf16*>(a.dout) + qoff + 8 * half;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             qop[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-            if constexpr (LO) qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
             gop[c] = *reinterpret_cast<const bf16x8*>(gr + 16 * c);
         }
     }
@@ -362,7 +430,13 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     const float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + rowc / kTile) * 2 * kTile;
     const float nlsc = ldt[ld_lsc(rowc % kTile)];      // -l'
     const float ndlt = ldt[ld_dlt(rowc % kTile)];      // -delta
-    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
+    const bool lo = flag != 0;
+    if (lo) {
+        const bf16* ql = reinterpret_cast<const bf16*>(a.qrot_lo) + qoff + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
+    }
+    wait_vmcnt<0>();   // operands, the first tile and the table rows (see copy16_to_lds)
 
     // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
@@ -378,100 +452,127 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     f32x16 dqt[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) dqt[i] = f32x16{};
-
-    int buf = 0;                                      // stage of the current step
-    for (int st = 0; st < nsteps; ++st) {
-        wait_vmcnt<0>();                     // this wave's copies of tile st, the only ones in flight
-        step_barrier();                      // tile st is complete; the other stage is free
-        if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
-        const int j0 = st * kTile;
-        if (j0 <= wq0 + 31) {               // some key of the tile is at or before some query of the wave
-            const bf16* Ks = S.k[buf];
-            const bf16* Vs = S.v[buf];
-            // key / value row fragments as one batch.  Then per 32-key half (kt) its score and dP
-            // products; L and delta are known, so a half's dS' needs only its own products: the
-            // softmax of half 0 is slotted between the products of half 1, and that of half 1
-            // between the dQ products of half 0, so that vector work and matrix products of one
-            // wave overlap
-            bf16x8 kf[2][NCH], vf[2][NCH];
+    // -l' as the starting value of the score products (one query per lane), so that the products
+    // themselves subtract it
+    f32x16 nl16;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+    for (int r = 0; r < 16; ++r) nl16[r] = nlsc;
+
+    // the step loop, with and without the low-part products
+    auto run = [&](auto lo_c) {
+        constexpr bool LO = decltype(lo_c)::value;
+        int buf = 0;                                  // stage of the current step
+        for (int st = 0; st < nsteps; ++st) {
+            wait_vmcnt<0>();                 // this wave's copies of tile st, the only ones in flight
+            step_barrier();                  // tile st is complete; the other stage is free
+            if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
+            const int j0 = st * kTile;
+            // the step's work; DIAG: the tile reaches past the wave's first query, so some of its
+            // keys come after some of the wave's queries and are masked (only there: the compare
+            // and select of the mask cost as many vector instructions as the softmax itself)
+            auto body = [&](auto diag_c) {
+                constexpr bool DIAG = decltype(diag_c)::value;
+                const bf16* Ks = S.k[buf];
+                const bf16* Vs = S.v[buf];
+                // Per 32-key half (kt): its key / value row fragments, then its score and dP products,
+                // the scores starting from -l' (the masked keys of a diagonal tile from -inf).  L
+                // and delta are known, so a half's dS' needs only its own products: the fragments of
+                // half 1 are read while the products of half 0 run, the softmax of half 0 is slotted
+                // between the products of half 1, and that of half 1 between the dQ products of half
+                // 0, so that vector work and matrix products of one wave overlap
+                auto sinit = [&](int kt) {
+                    if constexpr (DIAG) {
+                        f32x16 m;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) m[r] = j0 + 32 * kt + acc_row(r, half) > qrow ? -INFINITY : nlsc;
+                        return m;
+                    } else {
+                        return nl16;
+                    }
+                };
+                bf16x8 kf0[NCH], vf0[NCH];
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    kf[kt][c] = *reinterpret_cast<const bf16x8*>(Ks + roff[kt][c]);
-                    vf[kt][c] = *reinterpret_cast<const bf16x8*>(Vs + roff[kt][c]);
+                    kf0[c] = *reinterpret_cast<const bf16x8*>(Ks + roff[0][c]);
+                    vf0[c] = *reinterpret_cast<const bf16x8*>(Vs + roff[0][c]);
                 }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 sT[2], dpT[2];
-            sT[0] = M::mma(kf[0][0], qop[0], f32x16{});
-            dpT[0] = M::mma(vf[0][0], gop[0], f32x16{});
-            if constexpr (LO) sT[0] = M::mma(kf[0][0], qlo[0], sT[0]);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 sT[2], dpT[2];
+                sT[0] = M::mma(kf0[0], qop[0], sinit(0));
+                dpT[0] = M::mma(vf0[0], gop[0], f32x16{});
+                if constexpr (LO) sT[0] = M::mma(kf0[0], qlo[0], sT[0]);
 #pragma unroll
-            for (int c = 1; c < NCH; ++c) {
-                sT[0] = M::mma(kf[0][c], qop[c], sT[0]);
-                dpT[0] = M::mma(vf[0][c], gop[c], dpT[0]);
-                if constexpr (LO) sT[0] = M::mma(kf[0][c], qlo[c], sT[0]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 ktf[4][NDT];
-#pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_at<D>(Ks, ktb[dt], 16 * pc);
-            __builtin_amdgcn_sched_barrier(0);
-            // dS'^T = P' (dP^T - delta) of register group rg of half kt, packed into the B operand
-            // chunk 2 kt + rg / 2 (4 chunks of 16 keys)
-            bf16x8 sb[4];
-            const bool diag = j0 + kTile - 1 > wq0;
-            auto ds_group = [&](int kt, int rg) {
-                float d[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rg + e;
-                    float p = __builtin_amdgcn_exp2f(sT[kt][r] + nlsc);
-                    if (diag && j0 + 32 * kt + acc_row(r, half) > qrow) p = 0.f;
-                    d[e] = p * (dpT[kt][r] + ndlt);
+                for (int c = 1; c < NCH; ++c) {
+                    sT[0] = M::mma(kf0[c], qop[c], sT[0]);
+                    dpT[0] = M::mma(vf0[c], gop[c], dpT[0]);
+                    if constexpr (LO) sT[0] = M::mma(kf0[c], qlo[c], sT[0]);
                 }
-                const bf16x4 d4 = cvt4(d);
-                const int pc = 2 * kt + (rg >> 1);
-                if (rg & 1) sb[pc] = __builtin_shufflevector(sb[pc].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
-                else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 kf1[NCH], vf1[NCH], ktf[4][NDT];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    kf1[c] = *reinterpret_cast<const bf16x8*>(Ks + roff[1][c]);
+                    vf1[c] = *reinterpret_cast<const bf16x8*>(Vs + roff[1][c]);
+                }
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) ktf[pc][dt] = tr_frag_at<D>(Ks, ktb[dt], 16 * pc);
+                __builtin_amdgcn_sched_barrier(0);
+                // dS'^T = P' (dP^T - delta) of register group rg of half kt, packed into the B
+                // operand chunk 2 kt + rg / 2 (4 chunks of 16 keys)
+                bf16x8 sb[4];
+                auto ds_group = [&](int kt, int rg) {
+                    float d[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rg + e;
+                        d[e] = __builtin_amdgcn_exp2f(sT[kt][r]) * (dpT[kt][r] + ndlt);
+                    }
+                    const bf16x4 d4 = cvt4(d);
+                    const int pc = 2 * kt + (rg >> 1);
+                    if (rg & 1) sb[pc] = __builtin_shufflevector(sb[pc].lo, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    else sb[pc] = __builtin_shufflevector(d4, d4, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
+                // products of half 1, chunk by chunk, each followed by its share of half 0's groups
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    sT[1] = M::mma(kf1[c], qop[c], c == 0 ? sinit(1) : sT[1]);
+                    dpT[1] = M::mma(vf1[c], gop[c], c == 0 ? f32x16{} : dpT[1]);
+                    if constexpr (LO) sT[1] = M::mma(kf1[c], qlo[c], sT[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int rg = c * 4 / NCH; rg < (c + 1) * 4 / NCH; ++rg) ds_group(0, rg);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // dQ~^T (D x 32 queries) += K~^T dS'^T (K = the tile's keys, accumulator order):
+                // the chunks of half 0, each followed by two of half 1's groups, then those of half 1
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    ds_group(1, 2 * pc);
+                    ds_group(1, 2 * pc + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int pc = 2; pc < 4; ++pc)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
             };
-            // products of half 1, chunk by chunk, each followed by its share of half 0's groups
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                sT[1] = M::mma(kf[1][c], qop[c], c == 0 ? f32x16{} : sT[1]);
-                dpT[1] = M::mma(vf[1][c], gop[c], c == 0 ? f32x16{} : dpT[1]);
-                if constexpr (LO) sT[1] = M::mma(kf[1][c], qlo[c], sT[1]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int rg = c * 4 / NCH; rg < (c + 1) * 4 / NCH; ++rg) ds_group(0, rg);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // dQ~^T (D x 32 queries) += K~^T dS'^T (K = the tile's keys, accumulator order): the
-            // chunks of half 0, each followed by two of half 1's groups, then those of half 1
-#pragma unroll
-            for (int pc = 0; pc < 2; ++pc) {
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
-                __builtin_amdgcn_sched_barrier(0);
-                ds_group(1, 2 * pc);
-                ds_group(1, 2 * pc + 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int pc = 2; pc < 4; ++pc)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) dqt[dt] = M::mma(ktf[pc][dt], sb[pc], dqt[dt]);
+            if (j0 + kTile - 1 <= wq0) body(std::false_type{});
+            else if (j0 <= wq0 + 31) body(std::true_type{});   // some key at or before some query of the wave
+            buf ^= 1;
         }
-        buf ^= 1;
-    }
+    };
+    if (lo) run(std::true_type{});
+    else run(std::false_type{});
 
     // dQ = R^T dQ~ ; lane owns one query, 4 consecutive d per register group
     if (qrow < T_) {
-        const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) load_acc_cs<D>(a.rope_cs, qrow, half, cs);
+        if (rope) CsRows<D, kQBlk>::read(S.cs, 32 * w + col, half, cs);
         bf16* __restrict__ dq = reinterpret_cast<bf16*>(a.dq) + ((size_t)bh * T_ + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -483,28 +584,6 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
                 *reinterpret_cast<bf16x4*>(dq + d) = cvt4(x);
             }
     }
-}
-
-// A dK/dV block uses the low-part tiles when any query block it visits (those at or after its key
-// tile, every head of its group) has its flag set; its other steps then read zeros there.
-template <int D>
-__device__ void dkdv(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
-    const int G = a.Hq / a.Hkv;
-    const int nblk = (a.T + kQBlk - 1) / kQBlk;
-    const int I0 = jt / 2, nI = nblk - I0;
-    const int* lof = a.lof + (size_t)(bg / a.Hkv * a.Hq + bg % a.Hkv * G) * nblk;
-    int any = 0;
-    for (int idx = threadIdx.x & 63; idx < G * nI; idx += 64) any |= lof[(idx / nI) * nblk + I0 + idx % nI];
-    if (__builtin_amdgcn_ballot_w64(any != 0) != 0) dkdv_block<D, true>(a, S, jt, bg);
-    else dkdv_block<D, false>(a, S, jt, bg);
-}
-
-// A dQ block uses the low part when its own query block's flag is set (as the forward did).
-template <int D>
-__device__ void dq(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
-    const int nblk = (a.T + kQBlk - 1) / kQBlk;
-    if (a.lof[(size_t)bh * nblk + qt]) dq_block<D, true>(a, S, qt, bh);
-    else dq_block<D, false>(a, S, qt, bh);
 }
 
 // workgroups per CU the kernel is compiled for: two (≤ 256 registers per wave) up to head_dim 64;
@@ -527,19 +606,19 @@ __global__ __launch_bounds__(kThreads, BwdOcc<D>::MINB) void bwd_bf16_kernel(Bwd
         const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
         const int gpx = BG / kXcds;                     // kv groups per XCD
         if (j < nkv * gpx) {
-            dkdv<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
+            dkdv_block<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
         } else {
             const int r = j - nkv * gpx;
             const int per = gpx * G;
             const int bg = ((r % per) / G) * kXcds + x;
-            dq<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
+            dq_block<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
         }
     } else {
         const int BH = a.B * a.Hq;
         const int ndk = nkv * BG;
         const int blk = (int)blockIdx.x;
-        if (blk < ndk) dkdv<D>(a, S.kv, blk / BG, blk % BG);
-        else dq<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
+        if (blk < ndk) dkdv_block<D>(a, S.kv, blk / BG, blk % BG);
+        else dq_block<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
     }
 }
 

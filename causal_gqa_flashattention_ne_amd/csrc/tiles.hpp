@@ -133,7 +133,12 @@ __device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(l
 // per-lane operands a kernel loads before its step loop are waited for (vmcnt(0)) before the loop
 // starts, so no other vector-memory load is in flight in it.
 //
-// Wait states.  soff and the descriptor are scalar registers that a VALU instruction
+// Range.  soff is folded into the descriptor (base moved by soff, size cut by soff, never below
+// zero) and the instruction's own scalar offset is 0: the hardware's range check then covers the
+// whole offset voff + soff, so a read at or past the buffer's size writes zeros to LDS and never
+// touches memory past the buffer, however the check treats a scalar offset.
+//
+// Wait states.  The descriptor words and M0 are scalar registers that a VALU instruction
 // (v_readfirstlane) may have written just before this block, and the gfx9 family (gfx950
 // included) requires 5 wait states between a VALU write of an SGPR and a vector-memory
 // instruction that reads it; M0 written by a scalar move needs 1 before an LDS-direct load.  The
@@ -144,7 +149,13 @@ __device__ inline void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned soff, u
     // soff and lds are wave-uniform; readfirstlane puts them in scalar registers even where the
     // compiler kept a uniform value in a vector register
     const unsigned so = __builtin_amdgcn_readfirstlane(soff), m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(rsrc), "s"(so), "{m0}"(m0)
+    const unsigned lo = (unsigned)rsrc[0] + so;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)lo);
+    r[1] = __builtin_amdgcn_readfirstlane(rsrc[1] + (int)(lo < so));   // carry into address bits 32..47
+    r[2] = __builtin_amdgcn_readfirstlane((unsigned)rsrc[2] > so ? (int)((unsigned)rsrc[2] - so) : 0);
+    r[3] = rsrc[3];
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(r), "{m0}"(m0)
                  : "memory");
 }
 
