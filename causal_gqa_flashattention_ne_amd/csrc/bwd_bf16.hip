@@ -69,14 +69,12 @@ struct alignas(16) DkdvLds {
     alignas(16) bf16 ql[kBS][kTile * D];   // Q~ remainder tiles (lo part)
     alignas(16) bf16 g[kBS][kTile * D];    // dO tiles
     alignas(16) float ld[kBS][2 * kTile];  // l' and delta, see ld_lsc
-    alignas(16) float cs[kTile * D];       // RoPE table rows of the block's keys (CsRows layout)
 };
 
 template <int D>
 struct alignas(16) DqLds {
     alignas(16) bf16 k[kBS][kTile * D];    // K~ tiles [key][d]
     alignas(16) bf16 v[kBS][kTile * D];    // V tiles
-    alignas(16) float cs[kQBlk * D];       // RoPE table rows of the block's queries (CsRows layout)
 };
 
 template <int D>
@@ -85,42 +83,15 @@ union alignas(16) BwdLds {
     DqLds<D> q;
 };
 
-// ROWS rows of the RoPE table ((cos, sin) pairs, D floats per row) copied into LDS with the copy
-// instructions of the tiles, in the prologue, for the un-rotation in the epilogue; the 16-byte
-// chunk c of row r sits at chunk position c ^ (r mod D/4), so that the epilogue's reads (one row
-// per lane) are spread over the banks.  Rows past the table's end read as zeros.
-template <int D, int ROWS>
-struct CsRows {
-    static constexpr int CPR = D / 4, NU = ROWS * CPR / (64 * kWaves);
-    static_assert(NU >= 1 && (ROWS * CPR) % (64 * kWaves) == 0, "table chunks must cover the waves evenly");
-    __device__ static inline void copy(const float* cs, int T, int r0, unsigned lds, int w, int lane) {
-        const i32x4 rs = buffer_rsrc(cs, (unsigned)T * (unsigned)(D * 4));
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int idx = (u * kWaves + w) * 64 + lane, r = idx / CPR, c = (idx % CPR) ^ (r % CPR);
-            copy16_to_lds(rs, (unsigned)(r * D + 4 * c) * 4u, (unsigned)r0 * (unsigned)(D * 4), lds + (unsigned)(u * kWaves + w) * 1024u);
-        }
-    }
-    // element offset of (row r, d), d a multiple of 4 (one 16-byte chunk)
-    __device__ static inline int at(int r, int d) { return r * D + (((d >> 2) ^ (r % CPR)) << 2); }
-    // the table entries behind this lane's accumulator groups of row r (see load_acc_cs)
-    __device__ static inline void read(const float* S, int r, int half, f32x4 (&c)[D / 32][4]) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) c[dt][rq] = *reinterpret_cast<const f32x4*>(S + at(r, 32 * dt + acc_row(4 * rq, half)));
-    }
-};
-
 typedef const __attribute__((address_space(4))) int cint;   // loads through it are scalar loads
 
 // ---------------------------------------------------------------------------------------------
 // dK/dV block: keys [j0, j0 + 64) of kv head (b, g).
 //
 // Prologue: every load the block needs before its first step goes out together (the low-part
-// flags of the query blocks it meets, this lane's K~ / V rows, the first tiles, the RoPE rows of
-// the epilogue), so that the block waits for one memory round trip; only a block that uses the
-// low part then fetches its first remainder tile.
+// flags of the query blocks it meets, this lane's K~ / V rows, the first tiles), so that the block
+// waits for one memory round trip; only a block that uses the low part then fetches its first
+// remainder tile.
 template <int D>
 __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     using M = Mfma<bf16>;
@@ -181,8 +152,6 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         tc.copy(r, row0, lql + (unsigned)buf * TileCopy<D>::kBytes, w);
     };
     issue(0, 0, 0);
-    const bool rope = a.rope_cs != nullptr;
-    if (rope) CsRows<D, kTile>::copy(a.rope_cs, T_, j0, lds_addr(&S.cs[0]), w, lane);
 
     // this lane's key row: K~ and V as B operands
     bf16x8 kop[NCH], vop[NCH];
@@ -212,7 +181,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         return lofs[__builtin_amdgcn_readfirstlane(hh * nblk + I0 + i)];
     };
     if (lo) issue_lo(0, 0, 0, flag(0, 0));
-    wait_vmcnt<0>();   // operands, the first tiles and the table rows (see copy16_to_lds)
+    wait_vmcnt<0>();   // operands and the first tiles (see copy16_to_lds)
 
     // per-lane LDS offsets of the row fragments (query row 32*qh + col, chunks 2c + half)
     int roff[NCH];
@@ -352,8 +321,9 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     if (qh == 0 && key < T_) {
         const float inv_scale = 1.f / a.scale;     // dV was accumulated from P' = scale * P
         const float inv_c = 1.f / (a.scale * kLog2e);   // dK from Q~' = scale * log2(e) * Q~
+        const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) CsRows<D, kTile>::read(S.cs, kloc, half, cs);
+        if (rope) load_acc_cs<D>(a.rope_cs, key, half, cs);
         const size_t base = ((size_t)bg * T_ + key) * D;
         bf16* __restrict__ dk = reinterpret_cast<bf16*>(a.dk) + base;
         bf16* __restrict__ dv = reinterpret_cast<bf16*>(a.dv) + base;
@@ -378,8 +348,8 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
 // ---------------------------------------------------------------------------------------------
 // dQ block: queries [i0, i0 + 128) of query head (b, h).  As in the dK/dV block, the prologue's
 // loads (the block's low-part flag, the first key / value tiles, this lane's Q~' and dO rows and
-// (l', delta), the RoPE rows) go out together; a block that uses the low part (as the forward
-// did for it) then loads its remainder rows.
+// (l', delta)) go out together; a block that uses the low part (as the forward did for it) then
+// loads its remainder rows.
 template <int D>
 __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     using M = Mfma<bf16>;
@@ -412,8 +382,6 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         tc.copy(rv, row0, lv + so, w);
     };
     issue(0, 0);
-    const bool rope = a.rope_cs != nullptr;
-    if (rope) CsRows<D, kQBlk>::copy(a.rope_cs, T_, i0, lds_addr(&S.cs[0]), w, lane);
 
     // this lane's query row: Q~' (hi, and lo for a flagged block) and dO as B operands, -l' and -delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
@@ -436,7 +404,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
     }
-    wait_vmcnt<0>();   // operands, the first tile and the table rows (see copy16_to_lds)
+    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
@@ -571,8 +539,9 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 
     // dQ = R^T dQ~ ; lane owns one query, 4 consecutive d per register group
     if (qrow < T_) {
+        const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) CsRows<D, kQBlk>::read(S.cs, 32 * w + col, half, cs);
+        if (rope) load_acc_cs<D>(a.rope_cs, qrow, half, cs);
         bf16* __restrict__ dq = reinterpret_cast<bf16*>(a.dq) + ((size_t)bh * T_ + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -591,34 +560,65 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 template <int D> struct BwdOcc { static constexpr int MINB = 2; };
 template <> struct BwdOcc<128> { static constexpr int MINB = 1; };
 
+// block -> (key tile, kv group) of a dK/dV block, and -> (query tile, query head) of a dQ block.
+// Workgroups are dispatched round-robin over the XCDs: block i runs on XCD i % 8.  When the kv
+// groups divide evenly, all blocks of kv group bg (its dK/dV tiles and the dQ tiles of its query
+// heads) go to XCD bg % 8, so that the group's Q~, dO, K~ and V are fetched into one L2 only.
+// dK/dV blocks come key tile 0 first (it carries the most causal work), dQ blocks last query tile
+// first.
+__device__ inline void dkdv_index(int blk, int BG, int& jt, int& bg) {
+    if (BG % kXcds == 0) {
+        const int x = blk % kXcds, j = blk / kXcds, gpx = BG / kXcds;
+        jt = j / gpx;
+        bg = (j % gpx) * kXcds + x;
+    } else {
+        jt = blk / BG;
+        bg = blk % BG;
+    }
+}
+__device__ inline void dq_index(int blk, int BG, int G, int nqt, int& qt, int& bh) {
+    if (BG % kXcds == 0) {
+        const int x = blk % kXcds, r = blk / kXcds, per = BG / kXcds * G;
+        const int bg = ((r % per) / G) * kXcds + x;
+        qt = nqt - 1 - r / per;
+        bh = bg * G + (r % per) % G;
+    } else {
+        const int BH = BG * G;
+        qt = nqt - 1 - blk / BH;
+        bh = blk % BH;
+    }
+}
+
+// The two roles in one grid: the dK/dV blocks first, then the dQ blocks (each XCD gets its groups'
+// blocks of both roles in this order).
 template <int D>
 __global__ __launch_bounds__(kThreads, BwdOcc<D>::MINB) void bwd_bf16_kernel(BwdArgs a) {
     __shared__ BwdLds<D> S;
     const int BG = a.B * a.Hkv, G = a.Hq / a.Hkv;
     const int nkv = (a.T + kTile - 1) / kTile;
     const int nqt = (a.T + kQBlk - 1) / kQBlk;
+    const int ndk = nkv * BG;
+    int blk = (int)blockIdx.x;
     if (BG % kXcds == 0) {
-        // workgroups are dispatched round-robin over the XCDs: block i runs on XCD i % 8.  All
-        // blocks of kv group bg (its dK/dV tiles and the dQ tiles of its query heads) go to XCD
-        // bg % 8, so the group's Q~, dO, K~ and V are fetched into one L2 only.  Within an XCD:
-        // dK/dV blocks first (key tile 0 carries the most causal work), then dQ blocks (last
-        // query tile first).
-        const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
-        const int gpx = BG / kXcds;                     // kv groups per XCD
-        if (j < nkv * gpx) {
-            dkdv_block<D>(a, S.kv, j / gpx, (j % gpx) * kXcds + x);
+        // per XCD: its dK/dV blocks, then its dQ blocks
+        const int x = blk % kXcds, j = blk / kXcds, dpx = ndk / kXcds;
+        if (j < dpx) {
+            int jt, bg;
+            dkdv_index(j * kXcds + x, BG, jt, bg);
+            dkdv_block<D>(a, S.kv, jt, bg);
         } else {
-            const int r = j - nkv * gpx;
-            const int per = gpx * G;
-            const int bg = ((r % per) / G) * kXcds + x;
-            dq_block<D>(a, S.q, nqt - 1 - r / per, bg * G + (r % per) % G);
+            int qt, bh;
+            dq_index((j - dpx) * kXcds + x, BG, G, nqt, qt, bh);
+            dq_block<D>(a, S.q, qt, bh);
         }
+    } else if (blk < ndk) {
+        int jt, bg;
+        dkdv_index(blk, BG, jt, bg);
+        dkdv_block<D>(a, S.kv, jt, bg);
     } else {
-        const int BH = a.B * a.Hq;
-        const int ndk = nkv * BG;
-        const int blk = (int)blockIdx.x;
-        if (blk < ndk) dkdv_block<D>(a, S.kv, blk / BG, blk % BG);
-        else dq_block<D>(a, S.q, nqt - 1 - (blk - ndk) / BH, (blk - ndk) % BH);
+        int qt, bh;
+        dq_index(blk - ndk, BG, G, nqt, qt, bh);
+        dq_block<D>(a, S.q, qt, bh);
     }
 }
 
