@@ -635,8 +635,15 @@ __global__ __launch_bounds__(64) void decode16_kernel(DecodeArgs a, const int* _
     }
 
     // ---- pieces of shared segments: count the arrival; the last one merges ----
-    // The partial stores complete (vmcnt 0) before the count is raised, and the last arrival
-    // issues its loads only once the count has come back.
+    // Ordering across XCDs (whose L2 caches are not coherent with each other), with a relaxed
+    // counter: (1) the pieces were stored with sc1 (agent scope), which writes through this XCD's
+    // L2 to the memory side; (2) vmcnt(0) below waits until the memory side has acknowledged
+    // those stores; (3) only then is the counter raised, and an agent-scope atomic is performed at
+    // the memory side, after every earlier piece's own (1)-(2); (4) the wave that sees npieces - 1
+    // issues its loads after comparing that value (the empty asm keeps the compiler from hoisting
+    // them), and they are sc1 loads, which do not hit lines this XCD's L2 may hold from before.
+    // This is the agent-scope release / acquire of this family with the L2 write-back and
+    // invalidate replaced by the per-access sc1 policy on the lines that cross XCDs.
     wait_vmcnt<0>();
     int arrived[2] = {0, 0};                     // both counts raised before either is looked at
     if (lane == 0) {

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 7
+#define NE_ABI_VERSION 8
 
 enum {
     NE_OK = 0,
@@ -96,8 +96,11 @@ int ne_rope_table(int32_t rows, int32_t D, double theta, float* cs, void* stream
 int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, void* stream);
 
 /*
- * Bytes of workspace ne_attn_fwd needs for these parameters (0 on a bad shape, and 0 when none is
- * needed: float32, or no RoPE).  bf16 with RoPE: the keys rotated once per call, B*Hkv*T*D bf16.
+ * Bytes of workspace ne_attn_fwd needs for these parameters (0 on a bad shape, and 0 on the
+ * float32 path, which needs none).  bf16: the largest |k| of every 64-row key tile (float32,
+ * B*Hkv*ceil(T/64), rounded up to 256 bytes; it decides, per 128-query block, whether the rotated
+ * query's bf16 remainder enters the scores), then with RoPE the keys rotated once per call
+ * (B*Hkv*T*D bf16).  The bf16 forward therefore always takes a workspace.
  */
 size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p);
 
@@ -112,9 +115,12 @@ size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p);
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace that ne_attn_bwd needs for these parameters (0 on a bad shape): float32,
- * delta and float32 dQ, dK and dV accumulators; bf16, the per-row exponent offsets and deltas, the
- * rotated queries (two bf16 parts) and the rotated keys. */
+/* Bytes of workspace that ne_attn_bwd needs for these parameters (0 on a bad shape).  float32:
+ * delta, the dQ parts (one float32 [B,Hq,T,D] slice per 128-key tile, summed in key order) and the
+ * dK / dV parts (one slice per share of a key tile), so that the float32 backward is
+ * deterministic.  bf16: the per-row exponent offsets and deltas, the per-128-query-block flags of
+ * the query's low part, the largest |k| per 64-row key tile, the rotated queries scaled by
+ * scale*log2(e) (two bf16 parts) and the rotated keys. */
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);
 
 /*
@@ -137,9 +143,9 @@ int ne_attn_bwd(const ne_attn_params* p, const void* q, const void* k, const voi
  *
  * ne_attn_bwd_preprocess: delta_i = sum_d dout_id * o_id (float32) for every query row, the
  * per-row term of the softmax backward dS = P * (dP - delta), written into the workspace, which
- * it also prepares for ne_attn_bwd_main (float32: zeroed dQ, dK and dV accumulators; bf16: the rotated
- * queries R q and keys R k and, from lse, the per-row exponent offset).  Reads q, k, o, lse and
- * dout; writes only the workspace.
+ * it also prepares for ne_attn_bwd_main (bf16: the rotated queries R q and keys R k, the low-part
+ * flags made as the forward makes them and, from lse, the per-row exponent offset).  Reads q, k,
+ * o, lse and dout; writes only the workspace.
  *
  * ne_attn_bwd_main: dq, dk, dv as ne_attn_bwd, from a workspace that ne_attn_bwd_preprocess filled
  * for the same parameters, o and dout (stream order), with no call on that workspace in between.
