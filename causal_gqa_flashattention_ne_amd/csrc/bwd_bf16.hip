@@ -54,7 +54,6 @@ namespace {
 constexpr int kTile = kTileRows;       // keys per dK/dV block, queries per step; keys per dQ step
 constexpr int kQBlk = 128;             // queries per dQ block
 constexpr int kThreads = kBlockThreads;
-constexpr int kWaves = kBlockWaves;
 constexpr int kXcds = 8;               // accelerator complex dies of the MI355X, each with its own L2
 constexpr int kBS = 2;                 // LDS stages: a tile is fetched one step before its use
 
@@ -642,8 +641,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_bf16_kernel(BwdArgs a) {
     __shared__ float red[kThreads / 64];
     const int T_ = a.T;
     const int nblk = (T_ + kQBlk - 1) / kQBlk;
-    const long bh = (long)blockIdx.x / nblk;
-    const int I = (int)(blockIdx.x % nblk);
+    long bh;
+    int I;
+    {
+        // the rows of kv group bg go to XCD bg % 8, as the main kernel's blocks of that group do,
+        // so that the dO rows read here are still in that XCD's L2 when the main kernel runs
+        const int BG = a.B * a.Hkv, G = a.Hq / a.Hkv;
+        const int blk = (int)blockIdx.x;
+        if (BG % kXcds == 0) {
+            const int x = blk % kXcds, j = blk / kXcds, per = G * nblk;
+            bh = (long)((j / per) * kXcds + x) * G + (j % per) / nblk;
+            I = (j % per) % nblk;
+        } else {
+            bh = blk / nblk;
+            I = blk % nblk;
+        }
+    }
     const int tid = threadIdx.x;
     const size_t hbase = (size_t)bh * T_ * D;
     const bf16* __restrict__ o = reinterpret_cast<const bf16*>(a.o) + hbase;

@@ -363,7 +363,17 @@ __global__ __launch_bounds__(kThreads) void key_rot_kernel(KeyRotArgs a) {
     static_assert(NU >= 1 && kTile * CPR % kThreads == 0, "chunks must cover the threads evenly");
     __shared__ float red[kThreads / 64];
     const int ntile = (a.T + kTile - 1) / kTile;
-    const int bgi = (int)blockIdx.x / ntile, t = (int)blockIdx.x % ntile;
+    // the tiles of kv group bgi go to XCD bgi % 8, where the forward's blocks of that group read
+    // them
+    int bgi, t;
+    if (a.BH % kXcds == 0) {
+        const int x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+        bgi = (j / ntile) * kXcds + x;
+        t = j % ntile;
+    } else {
+        bgi = (int)blockIdx.x / ntile;
+        t = (int)blockIdx.x % ntile;
+    }
     const int tid = threadIdx.x;
     const size_t base = ((size_t)bgi * a.T + (size_t)t * kTile) * D;
     const bf16* __restrict__ k = reinterpret_cast<const bf16*>(a.k) + base;
@@ -415,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void key_rot_kernel(KeyRotArgs a) {
         float mm = red[0];
 #pragma unroll
         for (int i = 1; i < kThreads / 64; ++i) mm = fmaxf(mm, red[i]);
-        a.ak[blockIdx.x] = mm;
+        a.ak[(size_t)bgi * ntile + t] = mm;
     }
 }
 
