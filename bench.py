@@ -12,6 +12,9 @@ Prints ONE JSON line.  value = whole-job algorithmic TFLOP/s with the causal pai
 the same K steps run again with an event pair around every call (kernel_avg_us, which includes
 each pair's own overhead), then each call runs alone K times back to back between one event pair
 (kernel_alone_us); the roofline is that of the call with the longest alone time, at that time.
+Beside it: the FlashAttention-2-convention figure (7 B H T^2 D per layer), the step's algorithmic
+bytes per second against the HBM peak, and, with the CPU baseline, `parity`: the timed step's own
+layer-0 outputs against the oracle's on the sampled (batch, kv group) units, per output tensor.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
 
@@ -86,6 +89,13 @@ def host_info():
     except OSError:
         pass
     return {"host_cores": os.cpu_count(), "cpu_model": model}
+
+
+def device_info(torch, dev):
+    """The GPU's name, architecture and compute-unit count as the runtime reports them (the peaks
+    above are the published figures for 256 compute units)."""
+    pr = torch.cuda.get_device_properties(dev)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count}
 
 
 def kernel_bytes(w, elem):
@@ -241,6 +251,7 @@ def main():
     # ---- roofline of the dominant kernel ----
     kflops = {"fwd": 4.0 * w.D * pairs, "bwd_pre": 0.0, "bwd_main": 10.0 * w.D * pairs}
     kbytes = kernel_bytes(w, elem)
+    step_bytes = float(sum(kbytes.values())) * w.layers
     dom = max(alone_us, key=lambda kname: alone_us[kname])
     t_s = alone_us[dom] * 1e-6
     t_mfma = kflops[dom] / (peak * 1e12)
@@ -261,6 +272,7 @@ def main():
 
     # ---- CPU baseline: the oracle on the host cores (rank 0, N = 1 only) ----
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
         threads = args.cpu_threads or host_threads()
@@ -273,8 +285,23 @@ def main():
         sample = groups[:n]
         used = min(threads, n)
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, do, theta=w.theta, groups=sample, nthreads=used)
+        ref = oracle.attention(q, k, v, do, theta=w.theta, groups=sample, nthreads=used)
         dt = time.perf_counter() - t0
+        # the timed path's own layer-0 outputs (left in place by the last step) against the oracle
+        # on the sampled units: e(X) = max |X - X_ref| / max |X_ref| per output tensor
+        o0, lse0, dq0, dk0, dv0 = (t.float().cpu().numpy().astype(np.float64) for t in outs[0])
+        got = {"O": o0, "L": lse0, "dQ": dq0, "dK": dk0, "dV": dv0}
+        want = dict(zip(("O", "L", "dQ", "dK", "dV"), ref))
+        tol = 2e-2 if w.dtype == "bf16" else 1e-5
+        errs = {}
+        for name in got:
+            kv_side = name in ("dK", "dV")
+            sl = [(b, g) if kv_side else (b, slice(g * w.G, (g + 1) * w.G)) for b, g in sample]
+            diff = max(float(np.max(np.abs(got[name][i] - want[name][i]))) for i in sl)
+            scale = max(float(np.max(np.abs(want[name][i]))) for i in sl)
+            errs[name] = diff / scale if scale > 0 else diff
+        parity = {"max_rel_err": errs, "tol": tol, "pass": all(e <= tol for e in errs.values()),
+                  "sample": "the timed step's layer-0 outputs on the units of the CPU sample"}
         sample_flop = 14.0 * w.D * len(sample) * w.G * w.T * (w.T + 1) / 2
         cpu = {"value": sample_flop / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
                "sample": "%d of %d (batch, kv group) units of layer 0 (all %d query heads each, all T=%d "
@@ -306,10 +333,18 @@ def main():
                    "layers": w.layers, "causal": True, "rope_theta": w.theta, "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "peak_tflops": peak,
+        # FlashAttention-2's causal count, 7 B H T^2 D per layer (the value above counts the
+        # T(T+1)/2 pairs exactly)
+        "fa2_convention_tflops": 7.0 * w.B * w.Hq * w.T * w.T * w.D * w.layers / (ms_per_step * 1e-3) / 1e12,
+        # every tensor of the step read or written once, against the HBM peak
+        "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_pct_of_hbm_peak": 100.0 * step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "device": device_info(torch, dev),
         "kernel_avg_us": avg_us,
         "kernel_alone_us": alone_us,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(dev)
