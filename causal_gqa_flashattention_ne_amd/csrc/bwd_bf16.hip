@@ -74,6 +74,7 @@ template <int D>
 struct alignas(16) DqLds {
     alignas(16) bf16 k[kBS][kTile * D];    // K~ tiles [key][d]
     alignas(16) bf16 v[kBS][kTile * D];    // V tiles
+    alignas(16) bf16 xq[2][kTile * D];     // the block's Q~' rows in the prologue (two 64-row tiles)
 };
 
 template <int D>
@@ -151,18 +152,17 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         tc.copy(r, row0, lql + (unsigned)buf * TileCopy<D>::kBytes, w);
     };
     issue(0, 0, 0);
-
-    // this lane's key row: K~ and V as B operands
-    bf16x8 kop[NCH], vop[NCH];
+    // the block's 64 K~ and V rows, copied whole into the second stage's Q~ and dO tiles (unused
+    // until the second step's copies) and read from there into the operand layout: copies of
+    // contiguous rows take a quarter of the memory requests of per-lane row loads.  Rows past T
+    // read as zeros (those keys' results are not stored).
     {
-        const size_t off = ((size_t)bg * T_ + min(key, T_ - 1)) * D + 8 * half;
-        const bf16* kr = reinterpret_cast<const bf16*>(a.krot) + off;
-        const bf16* vr = reinterpret_cast<const bf16*>(a.v) + off;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            kop[c] = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
-            vop[c] = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
-        }
+        const unsigned kvbytes = (unsigned)T_ * (unsigned)(D * 2);
+        const size_t kvoff = (size_t)bg * T_ * D;
+        tc.copy(buffer_rsrc(reinterpret_cast<const bf16*>(a.krot) + kvoff, kvbytes), (unsigned)j0 * (unsigned)(D * 2),
+                lq + TileCopy<D>::kBytes, w);
+        tc.copy(buffer_rsrc(reinterpret_cast<const bf16*>(a.v) + kvoff, kvbytes), (unsigned)j0 * (unsigned)(D * 2),
+                lg + TileCopy<D>::kBytes, w);
     }
     // A block uses the low-part tiles when any query block it meets has its flag set; its other
     // steps then read zeros there.  With at most 64 such blocks their flags are one wave-uniform
@@ -180,7 +180,18 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         return lofs[__builtin_amdgcn_readfirstlane(hh * nblk + I0 + i)];
     };
     if (lo) issue_lo(0, 0, 0, flag(0, 0));
-    wait_vmcnt<0>();   // operands and the first tiles (see copy16_to_lds)
+    wait_vmcnt<0>();   // the key / value rows and the first tiles (see copy16_to_lds)
+    step_barrier();    // every wave's copies have landed
+
+    // this lane's key row: K~ and V as B operands
+    bf16x8 kop[NCH], vop[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int o = Swz<D>::at(kloc, 16 * c + 8 * half);
+        kop[c] = *reinterpret_cast<const bf16x8*>(&S.q[1][0] + o);
+        vop[c] = *reinterpret_cast<const bf16x8*>(&S.g[1][0] + o);
+    }
+    __syncthreads();   // every wave has its rows before the second step's copies overwrite them
 
     // per-lane LDS offsets of the row fragments (query row 32*qh + col, chunks 2c + half)
     int roff[NCH];
@@ -381,18 +392,24 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
         tc.copy(rv, row0, lv + so, w);
     };
     issue(0, 0);
+    // the block's 128 Q~' (hi) and dO rows, copied whole (Q~' into xq, dO into the second stage,
+    // unused until the second step's copies) and read from there into the operand layout, as the
+    // dK/dV block does with its key rows.  Rows past T read as zeros (not stored).
+    {
+        const unsigned qbytes = (unsigned)T_ * (unsigned)(D * 2);
+        const size_t hoff = (size_t)bh * T_ * D;
+        const i32x4 rq = buffer_rsrc(reinterpret_cast<const bf16*>(a.qrot) + hoff, qbytes);
+        const i32x4 rg = buffer_rsrc(reinterpret_cast<const bf16*>(a.dout) + hoff, qbytes);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const unsigned row0 = (unsigned)(i0 + t * kTile) * (unsigned)(D * 2);
+            tc.copy(rq, row0, lds_addr(&S.xq[t][0]), w);
+            tc.copy(rg, row0, t == 0 ? lk + TileCopy<D>::kBytes : lv + TileCopy<D>::kBytes, w);
+        }
+    }
 
     // this lane's query row: Q~' (hi, and lo for a flagged block) and dO as B operands, -l' and -delta
     bf16x8 qop[NCH], qlo[NCH], gop[NCH];
-    {
-        const bf16* qr = reinterpret_cast<const bf16*>(a.qrot) + qoff + 8 * half;
-        const bf16* gr = reinterpret_cast<const bf16*>(a.dout) + qoff + 8 * half;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            qop[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-            gop[c] = *reinterpret_cast<const bf16x8*>(gr + 16 * c);
-        }
-    }
     const int rowc = min(qrow, T_ - 1);
     const float* ldt = a.ld + ((size_t)bh * (a.Tp / kTile) + rowc / kTile) * 2 * kTile;
     const float nlsc = ldt[ld_lsc(rowc % kTile)];      // -l'
@@ -403,7 +420,19 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) qlo[c] = *reinterpret_cast<const bf16x8*>(ql + 16 * c);
     }
-    wait_vmcnt<0>();   // operands and the first tile (see copy16_to_lds)
+    wait_vmcnt<0>();   // the rows, (l', delta) and the first tile (see copy16_to_lds)
+    step_barrier();    // every wave's copies have landed
+    {
+        const bf16* xq = &S.xq[w >> 1][0];
+        const bf16* xg = (w >> 1) ? &S.v[1][0] : &S.k[1][0];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int o = Swz<D>::at(32 * (w & 1) + col, 16 * c + 8 * half);
+            qop[c] = *reinterpret_cast<const bf16x8*>(xq + o);
+            gop[c] = *reinterpret_cast<const bf16x8*>(xg + o);
+        }
+    }
+    __syncthreads();   // every wave has its rows before the second step's copies overwrite them
 
     // per-lane LDS offsets of the key / value row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
