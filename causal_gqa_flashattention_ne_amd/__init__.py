@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libne_attn.so")
 NE_OK = 0
 NE_DTYPE_F32 = 0
 NE_DTYPE_BF16 = 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 EXPORTS = ("ne_abi_version", "ne_status_string", "ne_rope_table", "ne_rope_apply", "ne_attn_fwd_workspace_bytes",
            "ne_attn_fwd", "ne_attn_bwd_workspace_bytes", "ne_attn_bwd", "ne_attn_bwd_preprocess", "ne_attn_bwd_main",

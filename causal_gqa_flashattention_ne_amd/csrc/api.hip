@@ -61,6 +61,11 @@ size_t delta_bytes(const ne_attn_params* p) {
 size_t key_bound_bytes(const ne_attn_params* p) {
     return ((size_t)p->B * p->Hkv * ((p->T + 63) / 64) * sizeof(float) + 255) & ~(size_t)255;
 }
+// bf16 with RoPE: the table's rows in the forward's query-operand order (rope_qcs_index), for whole
+// 64-row key tiles
+size_t qcs_bytes(const ne_attn_params* p) {
+    return p->rope_cs ? (size_t)((p->T + 63) / 64) * 64 * p->D * 2 * sizeof(float) : 0;
+}
 size_t lo_flag_bytes(const ne_attn_params* p) {
     return ((size_t)p->B * p->Hq * ((p->T + 127) / 128) * sizeof(int) + 255) & ~(size_t)255;
 }
@@ -299,8 +304,8 @@ size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p) {
     if (check_attn(p) != NE_OK) return 0;
     if (p->dtype != NE_DTYPE_BF16) return 0;
     // bf16: max |k| per 64-row key tile, then (with RoPE) the rotated keys, written once and read by
-    // every query head of their group
-    return key_bound_bytes(p) + (p->rope_cs ? (size_t)p->B * p->Hkv * p->T * p->D * 2 : 0);
+    // every query head of their group, and the table in the query-operand order
+    return key_bound_bytes(p) + (p->rope_cs ? (size_t)p->B * p->Hkv * p->T * p->D * 2 : 0) + qcs_bytes(p);
 }
 
 int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const void* v, void* o,
@@ -322,10 +327,15 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
             char* ws = static_cast<char*>(workspace);
             float* ak = reinterpret_cast<float*>(ws);
             void* krot = p->rope_cs ? ws + key_bound_bytes(p) : nullptr;
-            const hipError_t e = ne::launch_key_rot<DD>(ne::KeyRotArgs{k, krot, ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
+            float* qcs = p->rope_cs ? reinterpret_cast<float*>(ws + key_bound_bytes(p) +
+                                                               (size_t)p->B * p->Hkv * p->T * p->D * 2)
+                                    : nullptr;
+            const hipError_t e =
+                ne::launch_key_rot<DD>(ne::KeyRotArgs{k, krot, ak, p->rope_cs, p->B * p->Hkv, p->T, qcs}, s);
             if (e != hipSuccess) return e;
             if (krot) a.k = krot;
             a.ak = ak;
+            a.qcs = qcs;
             return ne::launch_fwd_bf16<DD>(a, s);
         } else {
             return ne::launch_fwd<T, DD>(a, s);
@@ -387,9 +397,10 @@ size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p) {
     // float32: delta | dQ parts, one slice per 128-key tile | dK and dV slices, one per share of a
     // key tile
     // bf16: (-l', -delta) per row | low-part flags | max |k| per key tile | scaled rotated Q hi | lo |
-    // rotated K
+    // rotated K | with RoPE, the table in the forward's query-operand order
     if (p->dtype == NE_DTYPE_BF16)
-        return delta_bytes(p) + lo_flag_bytes(p) + key_bound_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2;
+        return delta_bytes(p) + lo_flag_bytes(p) + key_bound_bytes(p) + 2 * ((qe * 2 + 255) & ~(size_t)255) + ke * 2 +
+               qcs_bytes(p);
     const size_t ns = (size_t)ne::bwd_f32_splits(p->B, p->Hq, p->Hkv, p->T);
     const size_t nkt = (size_t)(p->T + ne::kBwdF32Keys - 1) / ne::kBwdF32Keys;
     return delta_bytes(p) + (nkt * qe + 2 * ns * ke) * sizeof(float);
@@ -455,7 +466,7 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
         constexpr int DD = decltype(d)::value;
         if constexpr (std::is_same<T, ne::bf16>::value) {
             const hipError_t e = ne::launch_key_rot<DD>(
-                ne::KeyRotArgs{k, p->rope_cs ? a.krot : nullptr, a.ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
+                ne::KeyRotArgs{k, p->rope_cs ? a.krot : nullptr, a.ak, p->rope_cs, p->B * p->Hkv, p->T, nullptr}, s);
             if (e != hipSuccess) return e;
             return ne::launch_bwd_pre_bf16<DD>(a, s);
         } else {
@@ -473,8 +484,12 @@ int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, con
     if (int rc = bwd_args(p, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, &b))
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // with RoPE the table in the query-operand order follows the rotated keys
+    float* qcs = p->rope_cs ? reinterpret_cast<float*>(static_cast<char*>(b.krot) +
+                                                       (size_t)p->B * p->Hkv * p->T * p->D * 2)
+                            : nullptr;
     ne::FwdArgs a{q, b.krot, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p), b.qrot, b.qrot_lo,
-                  b.ak, b.lof};
+                  b.ak, b.lof, qcs};
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
@@ -482,7 +497,7 @@ int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, con
             // the keys as the backward reads them (rotated once here; without RoPE the raw keys)
             // and their tile bounds
             const hipError_t e = ne::launch_key_rot<DD>(
-                ne::KeyRotArgs{k, p->rope_cs ? b.krot : nullptr, b.ak, p->rope_cs, p->B * p->Hkv, p->T}, s);
+                ne::KeyRotArgs{k, p->rope_cs ? b.krot : nullptr, b.ak, p->rope_cs, p->B * p->Hkv, p->T, qcs}, s);
             if (e != hipSuccess) return e;
             return ne::launch_fwd_bf16<DD>(a, s);
         } else {

@@ -71,7 +71,8 @@ __device__ inline float wave_max(float x) {
 // The block's work once its precision is known.  qraw: this lane's raw query values (chunk c holds
 // d = 16c + 8*half + 0..7, row min(qrow, T-1)).
 template <int D, bool SAVE, bool LO>
-__device__ void fwd_block(const FwdArgs& a, FwdLds<D>& S, const bf16x8* qraw, int bg, int bh, int i0) {
+__device__ void fwd_block(const FwdArgs& a, FwdLds<D>& S, const bf16x8* qh_, const bf16x8* ql_, int bg, int bh,
+                          int i0) {
     using M = Mfma<bf16>;
     constexpr int NCH = D / 16, NDT = D / 32;
     const int T_ = a.T;
@@ -80,7 +81,6 @@ __device__ void fwd_block(const FwdArgs& a, FwdLds<D>& S, const bf16x8* qraw, in
     const int col = lane & 31, half = lane >> 5;
     const int wq0 = i0 + 32 * w;
     const int qrow = wq0 + col;
-    const float c2 = a.scale * kLog2e;
 
     const int kv_end = min(T_, i0 + kQBlk);
     const int nsteps = (kv_end + kTile - 1) / kTile;
@@ -97,27 +97,15 @@ __device__ void fwd_block(const FwdArgs& a, FwdLds<D>& S, const bf16x8* qraw, in
         tc.copy(rv, row0, lv + so, w);
     };
 
-    // this lane's query, rotated in float32, multiplied by scale*log2(e) and held as the bf16 B
-    // operand(s) of S'^T = K~ Q~'^T (hi, and with LO the remainder lo: the rotated query is then
-    // exact to ~2^-16 in the score product, and only the rounding of the rotated keys remains)
+    // this lane's query as the bf16 B operand(s) of S'^T = K~ Q~'^T (qh_ and, with LO, the
+    // remainder ql_: the rotated query is then exact to ~2^-16 in the score product, and only the
+    // rounding of the rotated keys remains)
     bf16x8 qhi[NCH], qlo[NCH];
-    {
-        const float* __restrict__ cs = a.rope_cs;
-        const int pos = min(qrow, T_ - 1);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)qraw[c][e];
-            if (cs) rope_rotate(x, 8, cs, D, pos, 16 * c + 8 * half, false);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= c2;
-            qhi[c] = cvt8(x);
-            if constexpr (LO) qlo[c] = remainder8(x, qhi[c]);
-        }
+    for (int c = 0; c < NCH; ++c) {
+        qhi[c] = qh_[c];
+        if constexpr (LO) qlo[c] = ql_[c];
     }
-
-    wait_vmcnt<0>();   // table entries and the first tile (see copy16_to_lds)
 
     // per-lane LDS offsets of the key row fragments (row 32*kt + col, chunks 2c + half)
     int roff[2][NCH];
@@ -314,15 +302,55 @@ __global__ __launch_bounds__(kThreads, FwdOcc<D>::MINB) void fwd_bf16_kernel(Fwd
 
     // this lane's raw query values and the block's precision: max |q| over the block's rows (a
     // wave reduction, then the 4 waves through LDS) against the largest max |k| of the key
-    // tiles the block visits
+    // tiles the block visits.  Up to head_dim 64 the 128 rows are copied whole into the second
+    // stage (unused until step 1) and read from there into the operand layout (copies of
+    // contiguous rows take a quarter of the memory requests of per-lane row loads; rows past T
+    // read as zeros, which leave max |q| unchanged and whose outputs are not stored), together
+    // with the first key / value tile and this lane's RoPE table entries in the query-operand
+    // order (one 16-byte piece per chunk and p): one round trip.  At head_dim 128 those entries,
+    // held through the barrier, would not fit the registers: the rows are loaded per lane and the
+    // tile and the entries follow the block maximum, as two round trips.
+    TileCopy<D> tc;
+    tc.init(w, lane);
+    const unsigned hbytes = (unsigned)T_ * (unsigned)(D * 2);
+    auto issue_tile0 = [&]() {
+        const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D, hbytes);
+        const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D, hbytes);
+        tc.copy(rk, 0u, lds_addr(&S.k[0][0]), w);
+        tc.copy(rv, 0u, lds_addr(&S.v[0][0]), w);
+    };
+    f32x4 tq[NCH][2];
+    auto load_tq = [&]() {
+        if (a.rope_cs) {
+            const f32x4* qcs = reinterpret_cast<const f32x4*>(a.qcs);
+            const int pos = min(qrow, T_ - 1);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) tq[c][p] = qcs[rope_qcs_index(pos, c, p, half, NCH)];
+        }
+    };
     bf16x8 qraw[NCH];
-    {
+    float km = 0.f;
+    if constexpr (D <= 64) {
+        const i32x4 rq = buffer_rsrc(reinterpret_cast<const bf16*>(a.q) + (size_t)bh * T_ * D, hbytes);
+        tc.copy(rq, (unsigned)i0 * (unsigned)(D * 2), lds_addr(&S.k[1][0]), w);
+        tc.copy(rq, (unsigned)(i0 + kTile) * (unsigned)(D * 2), lds_addr(&S.v[1][0]), w);
+        issue_tile0();
+        load_tq();
+        for (int j = lane; j < nsteps; j += 64) km = fmaxf(km, a.ak[(size_t)bg * ((T_ + kTile - 1) / kTile) + j]);
+        wait_vmcnt<0>();
+        step_barrier();                                 // every wave's copies have landed
+        const bf16* xq = (w >> 1) ? &S.v[1][0] : &S.k[1][0];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            qraw[c] = *reinterpret_cast<const bf16x8*>(xq + Swz<D>::at(32 * (w & 1) + col, 16 * c + 8 * half));
+    } else {
         const bf16* qr = reinterpret_cast<const bf16*>(a.q) + ((size_t)bh * T_ + min(qrow, T_ - 1)) * D + 8 * half;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) qraw[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+        for (int j = lane; j < nsteps; j += 64) km = fmaxf(km, a.ak[(size_t)bg * ((T_ + kTile - 1) / kTile) + j]);
     }
-    float km = 0.f;
-    for (int j = lane; j < nsteps; j += 64) km = fmaxf(km, a.ak[(size_t)bg * ((T_ + kTile - 1) / kTile) + j]);
     float qm = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
@@ -335,23 +363,43 @@ __global__ __launch_bounds__(kThreads, FwdOcc<D>::MINB) void fwd_bf16_kernel(Fwd
     float aq = S.red[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) aq = fmaxf(aq, S.red[i]);
-
-    // issue the first tile's copies before the query's rotation (its table loads)
-    {
-        const unsigned hbytes = (unsigned)T_ * (unsigned)(D * 2);
-        const i32x4 rk = buffer_rsrc(reinterpret_cast<const bf16*>(a.k) + (size_t)bg * T_ * D, hbytes);
-        const i32x4 rv = buffer_rsrc(reinterpret_cast<const bf16*>(a.v) + (size_t)bg * T_ * D, hbytes);
-        TileCopy<D> tc;
-        tc.init(w, lane);
-        tc.copy(rk, 0u, lds_addr(&S.k[0][0]), w);
-        tc.copy(rv, 0u, lds_addr(&S.v[0][0]), w);
+    if constexpr (D > 64) {
+        issue_tile0();
+        load_tq();
     }
+
     const bool lo = __builtin_amdgcn_readfirstlane((int)(a.scale * (float)D * aq * km > kLoBound)) != 0;
     if constexpr (SAVE) {
         if (tid == 0) a.lof[(size_t)bh * nqt + qt] = lo ? 1 : 0;
     }
-    if (lo) fwd_block<D, SAVE, true>(a, S, qraw, bg, bh, i0);
-    else fwd_block<D, SAVE, false>(a, S, qraw, bg, bh, i0);
+    // the query rotated in float32 and multiplied by scale*log2(e), as a bf16 part and, where the
+    // block's flag asks for it, its bf16 remainder
+    bf16x8 qhi[NCH], qlo[NCH];
+    {
+        const float c2 = a.scale * kLog2e;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)qraw[c][e];
+            if (a.rope_cs) {
+                const f32x4 t0 = tq[c][0], t1 = tq[c][1];
+                const float cc[4] = {t0[0], t0[2], t1[0], t1[2]}, ss[4] = {t0[1], t0[3], t1[1], t1[3]};
+#pragma unroll
+                for (int pr = 0; pr < 4; ++pr) {
+                    const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+                    x[2 * pr] = x0 * cc[pr] - x1 * ss[pr];
+                    x[2 * pr + 1] = x0 * ss[pr] + x1 * cc[pr];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= c2;
+            qhi[c] = cvt8(x);
+            if (lo) qlo[c] = remainder8(x, qhi[c]);
+        }
+    }
+    if (lo) fwd_block<D, SAVE, true>(a, S, qhi, qlo, bg, bh, i0);
+    else fwd_block<D, SAVE, false>(a, S, qhi, qlo, bg, bh, i0);
 }
 
 // Keys of one 64-row tile of (batch, kv head): K~ = R k (a copy without RoPE; nothing when krot is
@@ -406,6 +454,12 @@ __global__ __launch_bounds__(kThreads) void key_rot_kernel(KeyRotArgs a) {
             m = fmaxf(m, fabsf(y[e]));
         }
         if (a.rope_cs && a.krot) {
+            if (a.qcs && bgi == 0) {      // chunk `part` = operand chunk part / 2, lane half part % 2
+                const int row = t * kTile + r;
+                f32x4* q4 = reinterpret_cast<f32x4*>(a.qcs);
+                q4[rope_qcs_index(row, part >> 1, 0, part & 1, D / 16)] = c[u][0];
+                q4[rope_qcs_index(row, part >> 1, 1, part & 1, D / 16)] = c[u][1];
+            }
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
                 const float cc = c[u][pr / 2][2 * (pr % 2)], sn = c[u][pr / 2][2 * (pr % 2) + 1];

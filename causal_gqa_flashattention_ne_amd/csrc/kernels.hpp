@@ -27,7 +27,18 @@ struct FwdArgs {
                             // each; lo only for the blocks that use it), or nullptr
     const float* ak;        // bf16 kernel: [B, Hkv, ceil(T/64)] max |k| per key tile
     int* lof;               // bf16 kernel, training variant: [B, Hq, ceil(T/128)] low-part flags
+    const float* qcs;       // bf16 kernel with RoPE: the table's rows in the query-operand order
+                            // (rope_qcs_index), written by key_rot_kernel
 };
+
+// The RoPE table re-ordered for the bf16 forward's query rotation: the lane holding row r of a
+// 32-row wave (r % 32) in lane half h reads, for the 16 head_dim values of operand chunk c, the
+// (cos, sin) of pairs 8c + 4h + 2p and +1 (p = 0, 1) as one 16-byte piece.  Pieces are ordered
+// [r / 32][c][p][h][r % 32], so that each of a wave's loads reads 1 KB of contiguous memory;
+// ceil(T / 64) * 64 rows (rows past T are never read).
+inline constexpr size_t rope_qcs_index(int r, int c, int p, int h, int nch) {
+    return ((((size_t)(r >> 5) * nch + c) * 2 + p) * 2 + h) * 32 + (r & 31);   // in 16-byte pieces
+}
 
 // bf16 key rotation: K~ = R k (or a copy without RoPE) and ak64 per 64-row tile
 struct KeyRotArgs {
@@ -36,6 +47,8 @@ struct KeyRotArgs {
     float* ak;              // [B, Hkv, ceil(T/64)] max |k| per tile
     const float* rope_cs;   // or nullptr
     int BH, T;
+    float* qcs;             // or nullptr: the table in the query-operand order (rope_qcs_index),
+                            // written by the blocks of kv group 0
 };
 
 struct BwdArgs {

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 8
+#define NE_ABI_VERSION 9
 
 enum {
     NE_OK = 0,
@@ -100,7 +100,8 @@ int ne_rope_apply(const ne_rope_params* p, const void* x, void* y, int inverse, 
  * float32 path, which needs none).  bf16: the largest |k| of every 64-row key tile (float32,
  * B*Hkv*ceil(T/64), rounded up to 256 bytes; it decides, per 128-query block, whether the rotated
  * query's bf16 remainder enters the scores), then with RoPE the keys rotated once per call
- * (B*Hkv*T*D bf16).  The bf16 forward therefore always takes a workspace.
+ * (B*Hkv*T*D bf16) and the RoPE table's rows re-ordered for the query rotation (ceil(T/64)*64
+ * rows of D/2 float32 (cos, sin) pairs).  The bf16 forward therefore always takes a workspace.
  */
 size_t ne_attn_fwd_workspace_bytes(const ne_attn_params* p);
 
@@ -120,7 +121,8 @@ int ne_attn_fwd(const ne_attn_params* p, const void* q, const void* k, const voi
  * dK / dV parts (one slice per share of a key tile), so that the float32 backward is
  * deterministic.  bf16: the per-row exponent offsets and deltas, the per-128-query-block flags of
  * the query's low part, the largest |k| per 64-row key tile, the rotated queries scaled by
- * scale*log2(e) (two bf16 parts) and the rotated keys. */
+ * scale*log2(e) (two bf16 parts), the rotated keys and, with RoPE, the table rows re-ordered as in
+ * ne_attn_fwd_workspace_bytes (read by ne_attn_fwd_train). */
 size_t ne_attn_bwd_workspace_bytes(const ne_attn_params* p);
 
 /*

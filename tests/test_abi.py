@@ -122,6 +122,10 @@ def test_workspace_size_and_check():
     pl = params(B=8, Hq=8, Hkv=8, T=2048, D=64, dtype_code=ne.NE_DTYPE_F32)
     assert ne.bwd_workspace_bytes(pl) == 8 * 8 * 2048 * 4 + (16 * 8 * 8 + 2 * 8 * 8) * 2048 * 64 * 4
     assert bwd(p, ws_bytes=need - 1) == -5
+    # with RoPE the training pair's workspace also holds the re-ordered table
+    pr = params(B=2, Hq=4, Hkv=2, T=16, D=64)
+    pr.rope_cs, pr.rope_rows = ALIGNED, 16
+    assert ne.bwd_workspace_bytes(pr) == need + 64 * 64 * 2 * 4
 
 
 def test_rope_entry_points_validate():
@@ -149,7 +153,9 @@ def test_forward_workspace():
     assert fwd(p, ws=0) == -1
     p.rope_cs, p.rope_rows = ALIGNED, 16
     need = ne.fwd_workspace_bytes(p)
-    assert need == 256 + 2 * 2 * 16 * 64 * 2              # and the bf16 rotated keys, rotated once per call
+    # and the bf16 rotated keys, rotated once per call, and the RoPE table re-ordered for the query
+    # rotation (whole 64-row tiles of D/2 (cos, sin) float32 pairs)
+    assert need == 256 + 2 * 2 * 16 * 64 * 2 + 64 * 64 * 2 * 4
     assert fwd(p, ws=0) == -1
     assert fwd(p, ws=MISALIGNED) == -4
     assert fwd(p, ws_bytes=need - 1) == -5
