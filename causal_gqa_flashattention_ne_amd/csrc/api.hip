@@ -424,6 +424,7 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
     void* krot = nullptr;
     int* lof = nullptr;
     float* ak = nullptr;
+    float* qcs = nullptr;
     int nsplit = 1;
     if (p->dtype == NE_DTYPE_BF16) {
         const size_t qb = (qe * 2 + 255) & ~(size_t)255;
@@ -438,6 +439,8 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
         qrot_lo = x + qb;
         // without RoPE the kernels read the keys themselves
         krot = p->rope_cs ? x + 2 * qb : const_cast<void*>(k);
+        // with RoPE the table in the query-operand order follows the rotated keys
+        if (p->rope_cs) qcs = reinterpret_cast<float*>(x + 2 * qb + (size_t)p->B * p->Hkv * p->T * p->D * 2);
     } else {
         delta = reinterpret_cast<float*>(ws);
         const size_t ke = (size_t)p->B * p->Hkv * p->T * p->D;
@@ -447,7 +450,7 @@ int bwd_args(const ne_attn_params* p, const void* q, const void* k, const void* 
         dv_acc = dk_acc + (size_t)nsplit * ke;
     }
     *a = ne::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, delta, ld, dq_acc, dk_acc, dv_acc, qrot, qrot_lo, krot, p->rope_cs,
-                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p), nsplit, lof, ak};
+                     p->B, p->Hq, p->Hkv, p->T, padded_rows(p->T), eff_scale(p), nsplit, lof, ak, qcs};
     return NE_OK;
 }
 }  // namespace
@@ -466,7 +469,7 @@ int ne_attn_bwd_preprocess(const ne_attn_params* p, const void* q, const void* k
         constexpr int DD = decltype(d)::value;
         if constexpr (std::is_same<T, ne::bf16>::value) {
             const hipError_t e = ne::launch_key_rot<DD>(
-                ne::KeyRotArgs{k, p->rope_cs ? a.krot : nullptr, a.ak, p->rope_cs, p->B * p->Hkv, p->T, nullptr}, s);
+                ne::KeyRotArgs{k, p->rope_cs ? a.krot : nullptr, a.ak, p->rope_cs, p->B * p->Hkv, p->T, a.qcs}, s);
             if (e != hipSuccess) return e;
             return ne::launch_bwd_pre_bf16<DD>(a, s);
         } else {
@@ -484,12 +487,8 @@ int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, con
     if (int rc = bwd_args(p, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, &b))
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // with RoPE the table in the query-operand order follows the rotated keys
-    float* qcs = p->rope_cs ? reinterpret_cast<float*>(static_cast<char*>(b.krot) +
-                                                       (size_t)p->B * p->Hkv * p->T * p->D * 2)
-                            : nullptr;
     ne::FwdArgs a{q, b.krot, v, o, lse, p->rope_cs, p->B, p->Hq, p->Hkv, p->T, eff_scale(p), b.qrot, b.qrot_lo,
-                  b.ak, b.lof, qcs};
+                  b.ak, b.lof, b.qcs};
     return dispatch(p->dtype, p->D, [&](auto t, auto d) {
         using T = decltype(t);
         constexpr int DD = decltype(d)::value;
@@ -497,7 +496,7 @@ int ne_attn_fwd_train(const ne_attn_params* p, const void* q, const void* k, con
             // the keys as the backward reads them (rotated once here; without RoPE the raw keys)
             // and their tile bounds
             const hipError_t e = ne::launch_key_rot<DD>(
-                ne::KeyRotArgs{k, p->rope_cs ? b.krot : nullptr, b.ak, p->rope_cs, p->B * p->Hkv, p->T, qcs}, s);
+                ne::KeyRotArgs{k, p->rope_cs ? b.krot : nullptr, b.ak, p->rope_cs, p->B * p->Hkv, p->T, b.qcs}, s);
             if (e != hipSuccess) return e;
             return ne::launch_fwd_bf16<DD>(a, s);
         } else {

@@ -333,7 +333,7 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
         const float inv_c = 1.f / (a.scale * kLog2e);   // dK from Q~' = scale * log2(e) * Q~
         const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) load_acc_cs<D>(a.rope_cs, key, half, cs);
+        if (rope) load_acc_qcs<D>(a.qcs, key, half, cs);
         const size_t base = ((size_t)bg * T_ + key) * D;
         bf16* __restrict__ dk = reinterpret_cast<bf16*>(a.dk) + base;
         bf16* __restrict__ dv = reinterpret_cast<bf16*>(a.dv) + base;
@@ -569,7 +569,7 @@ __device__ void dq_block(const BwdArgs& a, DqLds<D>& S, int qt, int bh) {
     if (qrow < T_) {
         const bool rope = a.rope_cs != nullptr;
         f32x4 cs[NDT][4];
-        if (rope) load_acc_cs<D>(a.rope_cs, qrow, half, cs);
+        if (rope) load_acc_qcs<D>(a.qcs, qrow, half, cs);
         bf16* __restrict__ dq = reinterpret_cast<bf16*>(a.dq) + ((size_t)bh * T_ + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)

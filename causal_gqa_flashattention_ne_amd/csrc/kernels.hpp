@@ -82,6 +82,8 @@ struct BwdArgs {
     int* lof;               // bf16 path: [B, Hq, ceil(T/128)] 1 where a 128-row query block uses the
                             // rotated queries' low part (the forward's decision, kLoBound)
     float* ak;              // bf16 path: [B, Hkv, ceil(T/64)] max |k| per 64-row key tile
+    float* qcs;             // bf16 path with RoPE: the table in the query-operand order
+                            // (rope_qcs_index), written by key_rot_kernel; the epilogues read it
 };
 
 // float32 backward: each workgroup owns 128 keys of one (batch, kv head) and one of nsplit

@@ -9,6 +9,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace ne {
 
@@ -189,6 +190,18 @@ struct TileCopy {
 // (cos, sin) of the two RoPE pairs behind each 4-value group of a 32 x 32 accumulator column
 // held by this lane (row pos of the table; d = 32 dt + acc_row(4 rq, half) + 0..3): one 16-byte
 // load per group, all issued before any is used.
+// The same entries from the table re-ordered by rope_qcs_index: group (dt, rq) of lane half h
+// holds pairs 16 dt + 4 rq + 2 h + {0, 1}, the piece (chunk 2 dt + rq / 2, p = h, half rq % 2), so
+// that the 32 lanes of a lane half read 512 contiguous bytes per load.
+template <int D>
+__device__ inline void load_acc_qcs(const float* qcs, int pos, int half, f32x4 (&c)[D / 32][4]) {
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(qcs);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) c[dt][rq] = q4[rope_qcs_index(pos, 2 * dt + rq / 2, half, rq % 2, D / 16)];
+}
+
 template <int D>
 __device__ inline void load_acc_cs(const float* cs, int pos, int half, f32x4 (&c)[D / 32][4]) {
 #pragma unroll
