@@ -313,9 +313,14 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
     if (lo) run(std::true_type{});
     else run(std::false_type{});
 
+    // the RoPE entries of the key rows this wave stores, issued first so that they arrive during
+    // the reduction below (whose barriers are bare: __syncthreads would wait for these loads)
+    const bool rope = a.rope_cs != nullptr;
+    f32x4 cs[NDT][4];
+    if (rope && qh == 0) load_acc_qcs<D>(a.qcs, min(key, T_ - 1), half, cs);
     // add the two query halves' partial dK^T / dV^T through LDS (reuses the tile buffers once
-    // every wave is past its last step)
-    __syncthreads();
+    // every wave is past its last step: the loop's LDS reads have all been consumed by then)
+    step_barrier();
     float* red = reinterpret_cast<float*>(&S.q[0][0]);   // [dk|dv][kh][NDT][16 regs][64 lanes]
     static_assert(sizeof(S.q) + sizeof(S.ql) + sizeof(S.g) >= 2 * 2 * NDT * 16 * 64 * 4, "reduction buffer too small");
     if (qh == 1) {
@@ -327,13 +332,10 @@ __device__ void dkdv_block(const BwdArgs& a, DkdvLds<D>& S, int jt, int bg) {
                 red[(((2 + kh) * NDT + dt) * 16 + r) * 64 + lane] = dvt[dt][r];
             }
     }
-    __syncthreads();
+    step_barrier();   // (it waits for this wave's LDS writes, not for the loads above)
     if (qh == 0 && key < T_) {
         const float inv_scale = 1.f / a.scale;     // dV was accumulated from P' = scale * P
         const float inv_c = 1.f / (a.scale * kLog2e);   // dK from Q~' = scale * log2(e) * Q~
-        const bool rope = a.rope_cs != nullptr;
-        f32x4 cs[NDT][4];
-        if (rope) load_acc_qcs<D>(a.qcs, key, half, cs);
         const size_t base = ((size_t)bg * T_ + key) * D;
         bf16* __restrict__ dk = reinterpret_cast<bf16*>(a.dk) + base;
         bf16* __restrict__ dv = reinterpret_cast<bf16*>(a.dv) + base;
